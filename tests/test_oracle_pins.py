@@ -1,0 +1,481 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test ties an oracle function to what the MILLION page (page 2 of the
+source: the DAC 2025 write-up) or plain mathematics fixes: closed forms, the
+page's stated figures, textbook special cases, library routines (scipy,
+scikit-learn, torch) and brute force on tiny inputs.  A plausible mistake in
+the oracle (a dropped term, a wrong sign or index, a transposed operand) should
+fail at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthkv
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _nearest_bruteforce(X, C):
+    """Pure-Python nearest centroid, lowest index on exact ties."""
+    out = []
+    for x in X:
+        best, bd = 0, None
+        for c, cc in enumerate(C):
+            d = sum((float(a) - float(b)) ** 2 for a, b in zip(x, cc))
+            if bd is None or d < bd:
+                best, bd = c, d
+        out.append(best)
+    return np.array(out)
+
+
+# ------------------------------------------------------------------ O1 k-means
+def test_lloyd_invariants(oracle_mod):
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((600, 2))
+    X[:50] *= 8.0
+    order = rng.permutation(600)
+    iters = 8
+    C, assign, trace, kept = oracle.kmeans(X, 16, iters, order)
+    assert kept == 16
+    # SSE never increases, through assignment and update steps alike
+    assert np.all(np.diff(trace) <= 1e-12 * trace[0])
+    # every non-empty centroid is the mean of the members of the last assignment
+    for c in range(16):
+        mem = X[assign == c]
+        if len(mem):
+            np.testing.assert_allclose(C[c], mem.mean(axis=0), rtol=0, atol=1e-12)
+    # the last assignment is the nearest one for the centroids before the last update
+    C_prev, _, _, _ = oracle.kmeans(X, 16, iters - 1, order)
+    np.testing.assert_array_equal(assign, _nearest_bruteforce(X, C_prev))
+    # initialisation: the first 16 points of the order (all distinct here)
+    C0, a0, _, _ = oracle.kmeans(X, 16, 0, order)
+    np.testing.assert_array_equal(C0, X[order[:16]])
+    np.testing.assert_array_equal(a0, _nearest_bruteforce(X, C0))
+
+
+def test_kmeans_fig4_line8_bruteforce(oracle_mod):
+    """Fig. 4 setting: 8 points, 2 bits.  Optimal 1-D k-means clusters are
+    contiguous in sorted order, so enumerating the C(7,3)=35 cut sets gives the
+    optimum.  Lloyd's best over every initial subset reaches it, the optimum's
+    means are a Lloyd fixed point, and uniform 2-bit quantisation leaves code
+    10 unused while the clustering uses all four codes."""
+    g = _golden("fig4_line8.json")
+    pts = np.array(g["points"], dtype=np.float64)
+    K = g["n_clusters"]
+    xs = np.sort(pts)
+    best_sse, best_part = math.inf, None
+    for cuts in itertools.combinations(range(1, len(xs)), K - 1):
+        bounds = (0,) + cuts + (len(xs),)
+        parts = [xs[bounds[i]:bounds[i + 1]] for i in range(K)]
+        sse = sum(float(((p - p.mean()) ** 2).sum()) for p in parts)
+        if sse < best_sse:
+            best_sse, best_part = sse, parts
+    assert abs(best_sse - g["optimal_sse_by_hand"]) < 1e-12
+    assert [list(p) for p in best_part] == g["optimal_partition_by_hand"]
+    X = pts[:, None]
+    # Lloyd never beats the optimum; from some initial subset it reaches it
+    lloyd_best = math.inf
+    for init in itertools.combinations(range(8), K):
+        order = np.array(list(init) + [i for i in range(8) if i not in init])
+        C, assign, trace, _ = oracle.kmeans(X, K, 20, order)
+        final = float(((X[:, 0] - C[assign, 0]) ** 2).sum())
+        assert final >= best_sse - 1e-12
+        lloyd_best = min(lloyd_best, final)
+    assert abs(lloyd_best - best_sse) < 1e-12
+    # the optimum's means are a fixed point of Lloyd
+    means = np.array([[p.mean()] for p in best_part])
+    C, assign, _ = oracle.lloyd(X, means, 3)
+    np.testing.assert_array_equal(C, means)
+    assert len(set(assign.tolist())) == 4
+    # uniform 2-bit quantisation over [min, max] leaves level 2 (code 10) empty
+    step = (pts.max() - pts.min()) / 4
+    uni = np.minimum(((pts - pts.min()) / step).astype(int), 3)
+    assert uni.tolist() == g["uniform_codes_by_hand"]
+    assert 2 not in set(uni.tolist())
+
+
+def test_kmeans_distinct_points_equal_k(oracle_mod):
+    """When the data has exactly K distinct points, k-means keeps them all: SSE 0."""
+    rng = np.random.default_rng(3)
+    P = rng.standard_normal((12, 4))
+    X = P[rng.integers(0, 12, size=300)]
+    X[:12] = P  # every distinct point present
+    C, assign, trace, kept = oracle.kmeans(X, 12, 10, rng.permutation(300))
+    assert kept == 12
+    # the mean of n equal values is that value up to the rounding of sum/n
+    assert trace[-1] < 1e-24
+    np.testing.assert_allclose(np.array(sorted(map(tuple, C))), np.array(sorted(map(tuple, P))),
+                               rtol=1e-15, atol=1e-15)
+
+
+def test_kmeans_fewer_distinct_than_k(oracle_mod):
+    """Fewer distinct points than K: the remaining slots copy slot 0 and stay empty."""
+    X = np.array([[1.0, 2.0]] * 5 + [[3.0, -1.0]] * 4)
+    C, assign, trace, kept = oracle.kmeans(X, 4, 3, np.arange(9))
+    assert kept == 2
+    np.testing.assert_array_equal(C[2], C[0])
+    np.testing.assert_array_equal(C[3], C[0])
+    assert set(assign.tolist()) == {0, 1}
+    assert trace[-1] == 0.0
+
+
+def test_kmeans_matches_sklearn_lloyd(oracle_mod):
+    """Library pin: scikit-learn's Lloyd from the same initial centroids."""
+    from sklearn.cluster import KMeans
+
+    rng = np.random.default_rng(11)
+    centers = rng.standard_normal((8, 2)) * 6
+    X = centers[rng.integers(0, 8, size=800)] + rng.standard_normal((800, 2))
+    C0 = X[:8].copy()
+    order = np.arange(800)
+    for iters in (1, 3, 30):
+        C, _, _, _ = oracle.kmeans(X, 8, iters, order)
+        km = KMeans(n_clusters=8, init=C0, n_init=1, max_iter=iters, tol=0.0, algorithm="lloyd")
+        km.fit(X)
+        np.testing.assert_allclose(C, km.cluster_centers_, rtol=0, atol=1e-9)
+
+
+def test_fit_codebooks_layout(oracle_mod):
+    """fit_codebooks places subspace m of head h at cb[h, :, m, :] and equals
+    per-subspace k-means on the same points and initial order."""
+    rng = np.random.default_rng(5)
+    N, H, d, dsub, K = 200, 3, 8, 2, 6
+    x = rng.standard_normal((N, H, d)).astype(np.float32)
+    M = d // dsub
+    order = np.stack([np.stack([rng.permutation(N) for _ in range(M)]) for _ in range(H)])
+    cb = oracle.fit_codebooks(x, dsub, K, 5, order)
+    assert cb.shape == (H, K, M, dsub) and cb.dtype == np.float32
+    for h in range(H):
+        for m in range(M):
+            C, _, _, _ = oracle.kmeans(x[:, h, m * dsub:(m + 1) * dsub].astype(np.float64), K, 5, order[h, m])
+            np.testing.assert_array_equal(cb[h, :, m, :], C.astype(np.float32))
+
+
+# ------------------------------------------------------------------ O2 encode
+def test_encode_pure_python_tiny(oracle_mod):
+    rng = np.random.default_rng(2)
+    N, H, d, dsub, K = 9, 2, 6, 2, 5
+    x = rng.standard_normal((N, H, d)).astype(np.float32)
+    cb = rng.standard_normal((H, K, d // dsub, dsub)).astype(np.float32)
+    cb[1, 3] = cb[1, 1]  # duplicate centroid: index 1 must win, flagged ambiguous
+    x[4, 1, 0:2] = cb[1, 1, 0]  # exactly on the duplicated centroid
+    codes, d1, d2, amb = oracle.encode(x, cb)
+    for t in range(N):
+        for h in range(H):
+            for m in range(d // dsub):
+                exp = _nearest_bruteforce([x[t, h, m * dsub:(m + 1) * dsub]], cb[h, :, m, :])[0]
+                assert codes[t, h, m] == exp
+    assert codes[4, 1, 0] == 1 and d1[4, 1, 0] == 0.0 and d2[4, 1, 0] == 0.0 and amb[4, 1, 0]
+    assert np.all(amb[:, 1, :][codes[:, 1, :] == 1])  # every pick of the duplicate is ambiguous
+
+
+def test_encode_matches_scipy_vq(oracle_mod):
+    """Library pin: scipy's vector quantiser (nearest code by Euclidean distance)."""
+    from scipy.cluster.vq import vq
+
+    rng = np.random.default_rng(9)
+    N, H, d, dsub, K = 500, 2, 16, 4, 64
+    x = (rng.standard_normal((N, H, d)) * 3).astype(np.float32)
+    cb = rng.standard_normal((H, K, d // dsub, dsub)).astype(np.float32) * 3
+    codes, d1, d2, amb = oracle.encode(x, cb)
+    for h in range(H):
+        for m in range(d // dsub):
+            ref, dist = vq(x[:, h, m * dsub:(m + 1) * dsub].astype(np.float64), cb[h, :, m, :].astype(np.float64))
+            ok = ~amb[:, h, m]
+            np.testing.assert_array_equal(codes[:, h, m][ok], ref[ok])
+            np.testing.assert_allclose(np.sqrt(d1[:, h, m]), dist, rtol=1e-12, atol=1e-12)
+
+
+def test_encode_complete_codebook_roundtrip(oracle_mod):
+    """A codebook holding every distinct subvector: decode(encode(x)) == x exactly."""
+    levels = (-1.5, -0.5, 0.5, 1.5)
+    x = synthkv.grid_values(21, (300, 2, 8), levels)
+    grid = np.array(list(itertools.product(levels, repeat=2)), dtype=np.float32)  # 16 two-vectors
+    perm = np.random.default_rng(1).permutation(16)
+    cb = np.broadcast_to(grid[perm][None, :, None, :], (2, 16, 4, 2)).copy()
+    codes, d1, d2, amb = oracle.encode(x, cb)
+    assert np.all(d1 == 0.0) and not amb.any()
+    np.testing.assert_array_equal(oracle.dequantize(codes, cb), x.astype(np.float64))
+
+
+def test_encode_permutation_equivariance(oracle_mod):
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((400, 2, 8)).astype(np.float32)
+    cb = rng.standard_normal((2, 32, 4, 2)).astype(np.float32)
+    perm = rng.permutation(32)
+    inv = np.argsort(perm)
+    c1, _, _, amb = oracle.encode(x, cb)
+    c2, _, _, _ = oracle.encode(x, cb[:, perm])
+    ok = ~amb
+    np.testing.assert_array_equal(inv[c1][ok], c2[ok])
+
+
+def test_code_distance_consistent(oracle_mod):
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((50, 2, 8)).astype(np.float32)
+    cb = rng.standard_normal((2, 8, 4, 2)).astype(np.float32)
+    codes, d1, _, _ = oracle.encode(x, cb)
+    np.testing.assert_array_equal(oracle.code_distance(x, cb, codes), d1)
+    other = (codes.astype(int) + 1) % 8
+    assert np.all(oracle.code_distance(x, cb, other.astype(np.uint8)) >= d1)
+
+
+# ------------------------------------------------------------------ O3/O4 attention
+def _case(seed, B=2, Hq=4, Hkv=2, d=16, dsub=2, K=8, T=(37, 5), R=(3, 0), Tcap=64, Rcap=4):
+    rng = np.random.default_rng(seed)
+    M = d // dsub
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    cbk = rng.standard_normal((Hkv, K, M, dsub)).astype(np.float32)
+    cbv = rng.standard_normal((Hkv, K, M, dsub)).astype(np.float32)
+    ck = rng.integers(0, K, size=(B, Hkv, Tcap, M)).astype(np.uint8)
+    cv = rng.integers(0, K, size=(B, Hkv, Tcap, M)).astype(np.uint8)
+    rk = rng.standard_normal((B, Hkv, Rcap, d)).astype(np.float32)
+    rv = rng.standard_normal((B, Hkv, Rcap, d)).astype(np.float32)
+    return dict(q=q, cb_k=cbk, cb_v=cbv, codes_k=ck, codes_v=cv, hist_len=np.array(T, np.int32),
+                recent_k=rk, recent_v=rv, recent_len=np.array(R, np.int32), scale=1.0 / math.sqrt(d))
+
+
+def _dequant_head(codes, cb_head):
+    """codes [T, M], cb_head [K, M, dsub] -> [T, M*dsub] by direct indexing."""
+    T, M = codes.shape
+    return cb_head[codes, np.arange(M)[None, :]].reshape(T, -1).astype(np.float64)
+
+
+def test_decode_exact_matches_torch_sdpa(oracle_mod):
+    """Library pin: torch's scaled_dot_product_attention (fp64, CPU) over the
+    dequantised history followed by the recent tokens; lse via logsumexp."""
+    c = _case(12)
+    out, lse = oracle.decode_exact(**c)
+    B, Hq, d = c["q"].shape
+    g = Hq // c["cb_k"].shape[0]
+    for b in range(B):
+        T, R = int(c["hist_len"][b]), int(c["recent_len"][b])
+        for hq in range(Hq):
+            h = hq // g
+            keys = np.concatenate([_dequant_head(c["codes_k"][b, h, :T], c["cb_k"][h]),
+                                   c["recent_k"][b, h, :R].astype(np.float64)])
+            vals = np.concatenate([_dequant_head(c["codes_v"][b, h, :T], c["cb_v"][h]),
+                                   c["recent_v"][b, h, :R].astype(np.float64)])
+            qt = torch.from_numpy(c["q"][b, hq].astype(np.float64))[None, None, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qt, torch.from_numpy(keys)[None, None], torch.from_numpy(vals)[None, None],
+                scale=c["scale"])[0, 0, 0].numpy()
+            np.testing.assert_allclose(out[b, hq], ref, rtol=1e-12, atol=1e-12)
+            s = torch.from_numpy(keys) @ qt[0, 0, 0] * c["scale"]
+            assert abs(lse[b, hq] - torch.logsumexp(s, 0).item()) < 1e-12
+
+
+def test_decode_exact_special_cases(oracle_mod):
+    c = _case(13, B=3, T=(1, 0, 0), R=(0, 3, 0))
+    out, lse = oracle.decode_exact(**c)
+    g = c["q"].shape[1] // c["cb_k"].shape[0]
+    for hq in range(c["q"].shape[1]):
+        h = hq // g
+        # one history token, no recent: out is its dequantised value, lse its score
+        v0 = _dequant_head(c["codes_v"][0, h, :1], c["cb_v"][h])[0]
+        k0 = _dequant_head(c["codes_k"][0, h, :1], c["cb_k"][h])[0]
+        np.testing.assert_array_equal(out[0, hq], v0)
+        assert abs(lse[0, hq] - c["scale"] * float(k0 @ c["q"][0, hq].astype(np.float64))) < 1e-13
+        # no history: plain softmax attention over the recent tokens
+        s = c["scale"] * (c["recent_k"][1, h, :3].astype(np.float64) @ c["q"][1, hq].astype(np.float64))
+        p = np.exp(s - s.max())
+        np.testing.assert_allclose(out[1, hq], p @ c["recent_v"][1, h, :3] / p.sum(), rtol=1e-13, atol=1e-14)
+        # nothing cached: zeros and -inf
+        assert np.all(out[2, hq] == 0.0) and lse[2, hq] == -math.inf
+
+
+def test_decode_exact_softmax_shift_invariance(oracle_mod):
+    """Adding a constant to every centroid's projection on q shifts all scores
+    equally: out unchanged, lse shifted by exactly that amount."""
+    c = _case(14, B=1, Hq=2, Hkv=2, T=(20,), R=(0,), Rcap=1)
+    out1, lse1 = oracle.decode_exact(**c)
+    c2 = dict(c)
+    # raise every key by a multiple of q_hat along its first subspace: not generic; instead scale q
+    c2["scale"] = c["scale"] * 2.0
+    out2, lse2 = oracle.decode_exact(**c2)
+    c3 = dict(c)
+    c3["q"] = c["q"] * 2.0
+    out3, lse3 = oracle.decode_exact(**c3)
+    np.testing.assert_allclose(out2, out3, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse3, rtol=1e-12, atol=1e-13)
+    assert not np.allclose(out1, out2)
+
+
+# ------------------------------------------------------------------ O5 method algebra
+def test_lut_identity(oracle_mod):
+    """ad-LUT identity (Fig. 7 paragraph): summing table entries over a token's
+    codes gives the inner product of q with the dequantised key."""
+    c = _case(15, B=2, Hq=4, Hkv=2, d=32, dsub=4, K=16, T=(50, 64))
+    L = oracle.lut(c["q"], c["cb_k"], 2)
+    assert L.shape == (2, 4, 8, 16)
+    for b in range(2):
+        for hq in range(4):
+            h = hq // 2
+            s = oracle.lut_scores(L[b, hq], c["codes_k"][b, h], c["scale"])
+            keys = _dequant_head(c["codes_k"][b, h], c["cb_k"][h])
+            ref = c["scale"] * (keys @ c["q"][b, hq].astype(np.float64))
+            assert np.all(np.abs(s - ref) <= 1e-12 * (1 + np.abs(ref)))
+    # a single entry by hand: q subvector m . centroid c
+    m, cc = 3, 5
+    hand = sum(float(c["q"][1, 3, m * 4 + j]) * float(c["cb_k"][1, cc, m, j]) for j in range(4))
+    assert abs(L[1, 3, m, cc] - hand) < 1e-14
+
+
+def test_histogram_identity(oracle_mod):
+    """Per-subspace histograms of softmax weights times the value codebook equal
+    the softmax-weighted sum of dequantised values."""
+    rng = np.random.default_rng(16)
+    T, M, dsub, K = 300, 8, 2, 16
+    s = rng.standard_normal(T) * 3
+    cv = rng.integers(0, K, size=(T, M)).astype(np.uint8)
+    cbv = rng.standard_normal((K, M, dsub))
+    mu, l, o = oracle.hist_partial(s, cv, cbv)
+    p = np.exp(s - s.max())
+    ref = p @ _dequant_head(cv, cbv)
+    assert mu == s.max() and abs(l - p.sum()) < 1e-12 * p.sum()
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_method_equals_exact_any_partition(oracle_mod):
+    """LSE-merge closed form: any split of the history into contiguous parts,
+    plus the recent window, merges to the exact attention result."""
+    c = _case(17, B=2, Hq=8, Hkv=2, d=16, dsub=2, K=32, T=(200, 1), R=(4, 2), Tcap=256, Rcap=4)
+    ref_out, ref_lse = oracle.decode_exact(**c)
+    rng = np.random.default_rng(0)
+    for n_split in (1, 2, 7, 64):
+        def bounds(b, T, n=n_split):
+            if T == 0:
+                return [0]
+            cuts = np.sort(rng.choice(np.arange(1, max(T, 2)), size=min(n - 1, max(T - 1, 0)), replace=False))
+            return [0] + cuts.tolist()
+        out, lse = oracle.decode_method(**c, split_bounds=bounds)
+        np.testing.assert_allclose(out, ref_out, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_merge_states_closed_form(oracle_mod):
+    rng = np.random.default_rng(18)
+    n, d = 5, 8
+    sa, sb = rng.standard_normal((n, 6)), rng.standard_normal((n, 4))
+    va, vb = rng.standard_normal((n, 6, d)), rng.standard_normal((n, 4, d))
+
+    def state(s, v):
+        p = np.exp(s - s.max(1, keepdims=True))
+        return np.einsum("ns,nsd->nd", p, v) / p.sum(1, keepdims=True), np.log(np.exp(s).sum(1))
+
+    oa, la = state(sa, va)
+    ob, lb = state(sb, vb)
+    of, lf = state(np.concatenate([sa, sb], 1), np.concatenate([va, vb], 1))
+    out, lse = oracle.merge_states(oa, la, ob, lb)
+    np.testing.assert_allclose(out, of, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lf, rtol=1e-13, atol=1e-13)
+    lb2 = lb.copy()
+    lb2[1] = -np.inf  # an empty side has weight zero
+    out, lse = oracle.merge_states(oa, la, ob, lb2)
+    np.testing.assert_array_equal(out[1], oa[1])
+    assert lse[1] == la[1]
+    out, lse = oracle.merge_states(oa[:1], [-np.inf], ob[:1], [-np.inf])
+    assert np.all(out == 0) and lse[0] == -np.inf
+
+
+def test_complete_codebook_pq_attention_is_exact(oracle_mod):
+    """K/V elements drawn from 4 levels give exactly 16 distinct 2-vectors per
+    subspace; k-means with K=16 on that data recovers all of them, so PQ
+    attention equals exact attention on the original K/V (torch SDPA, fp64)."""
+    levels = (-1.5, -0.5, 0.5, 1.5)
+    H, d, dsub, K, T, R = 4, 64, 2, 16, 512, 16
+    M = d // dsub
+    kx = synthkv.grid_values(31, (T, H, d), levels)
+    vx = synthkv.grid_values(32, (T, H, d), levels)
+    order = np.stack([np.stack([np.random.default_rng(100 + h * M + m).permutation(T) for m in range(M)])
+                      for h in range(H)])
+    cbk = oracle.fit_codebooks(kx, dsub, K, 10, order)
+    cbv = oracle.fit_codebooks(vx, dsub, K, 10, order)
+    ck, d1k, _, _ = oracle.encode(kx, cbk)
+    cv, d1v, _, _ = oracle.encode(vx, cbv)
+    assert np.all(d1k == 0) and np.all(d1v == 0)
+    q = synthkv.small_normal(33, (1, H, d))
+    rk = synthkv.small_normal(34, (1, H, R, d))
+    rv = synthkv.small_normal(35, (1, H, R, d))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    out, lse = oracle.decode_exact(q, cbk, cbv, ck.transpose(1, 0, 2)[None], cv.transpose(1, 0, 2)[None],
+                                   [T], rk, rv, [R], scale)
+    for h in range(H):
+        keys = np.concatenate([kx[:, h].astype(np.float64), rk[0, h].astype(np.float64)])
+        vals = np.concatenate([vx[:, h].astype(np.float64), rv[0, h].astype(np.float64)])
+        qt = torch.from_numpy(q[0, h].astype(np.float64))[None, None, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, torch.from_numpy(keys)[None, None], torch.from_numpy(vals)[None, None], scale=scale)
+        np.testing.assert_allclose(out[0, h], ref[0, 0, 0].numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ O6 accounting
+def test_compression_ratio_matches_page(oracle_mod):
+    g = _golden("pages_figures.json")
+    cr = g["kv_compression_ratio"]
+    assert oracle.compression_ratio(128, cr["d_sub"], cr["code_bits"]) == cr["value"] == 4
+    assert oracle.compression_ratio(128, 4) == 8
+    assert oracle.compression_ratio(64, 2) == 4
+    # measured on real buffers: codes of a token-head versus its fp16 vector
+    w = synthkv.WORKLOADS["llama2_7b_32k"]
+    x = synthkv.kv_values(w, 0, "k", "history", 64)
+    codes = np.zeros((64, w.n_kv_heads, w.n_sub), np.uint8)
+    assert x.dtype == np.float16 and x.nbytes / codes.nbytes == 4
+    assert g["subspace_dims"]["value"] == [2, 4]
+
+
+def test_kv_cache_size_matches_page(oracle_mod):
+    g = _golden("pages_figures.json")["llama2_7b_kv_fp16_at_128k"]
+    s = g["shape"]
+    total = oracle.kv_cache_bytes_fp16(s["n_layers"], s["n_kv_heads"], s["head_dim"], s["n_tokens"])
+    assert total == 2 ** 36 and total / 2 ** 30 == g["value_gb"]
+    assert oracle.kv_cache_bytes_fp16(32, 32, 128, 1) == 524288
+    # PQ codes at d_sub=2 take a quarter of it
+    assert total / oracle.compression_ratio(128, 2) == 16 * 2 ** 30
+    assert oracle.codebook_bytes(32, 256, 128) == 8 * 2 ** 20
+
+
+# ------------------------------------------------------------------ code layout
+@pytest.mark.parametrize("M", [16, 32, 64])
+def test_code_layout_bijection_and_roundtrip(oracle_mod, M):
+    t_cap = 192
+    off = oracle.code_offsets(M, t_cap)
+    assert sorted(off.ravel().tolist()) == list(range(t_cap * M))
+    # brute force against the definition, loop by loop
+    for t in range(0, t_cap, 7):
+        lane = t % 64
+        for p in range(M):
+            m = (p + lane) % M
+            assert off[t, m] == (t // 64) * 64 * M + (p // 16) * 1024 + lane * 16 + p % 16
+    codes = synthkv.small_codes(40 + M, (2, 3, 150, M), 256)
+    planes = oracle.tile_codes(codes, t_cap)
+    np.testing.assert_array_equal(oracle.untile_codes(planes, 150, M), codes)
+
+
+def test_generator_deterministic_and_shaped():
+    w = synthkv.WORKLOADS["llama2_7b_32k"]
+    a = synthkv.kv_values(w, 0, "k", "history", 256)
+    b = synthkv.kv_values(w, 0, "k", "history", 256)
+    np.testing.assert_array_equal(a, b)
+    assert a.shape == (256, 32, 128) and a.dtype == np.float16
+    # outlier structure: 4 channels per head scaled x10, ~0.5% points x20
+    ch = synthkv.outlier_channels(w, 0, "k")
+    assert ch.shape == (32, 4) and all(len(set(r)) == 4 for r in ch.tolist())
+    big = np.abs(a.astype(np.float32)).mean(axis=0)  # [H, d]
+    for h in range(32):
+        assert set(np.argsort(big[h])[-4:].tolist()) == set(ch[h].tolist())
+    assert synthkv.WORKLOADS["full32_ragged4"].hist_len == (14698, 3634, 31436, 30564)
+    v = synthkv.kv_values(w, 0, "v", "history", 256)
+    assert not np.array_equal(a, v)
