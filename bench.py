@@ -1,0 +1,223 @@
+"""Benchmark: PQ decode attention KV tokens/s and % of HBM peak at 32K context, plus pq_encode tokens/s.
+
+Workload (N=1): LLaMA-2-7B-shaped decode layer -- batch 1, 32 heads x 128, d_sub=2,
+K=256 centroids, 32768 PQ history tokens + 128 fp16 recent tokens, K/V fp16 N(0,1)
+with 4 outlier channels per head scaled x10 and 0.5% point outliers x20 (synthkv).
+
+One step = one pqkv_decode_attention call: ad-LUT build, LUT-sum scoring of the
+history, split softmax with the histogram value side, recent-window attention and
+the log-sum-exp merge.  Inputs are resident in HBM; the timed loop rotates over
+--copies independent copies of the code planes, queries and recent window so the
+working set (>= 1 GiB) does not sit in the 256 MiB last-level cache.
+
+pq_encode is timed in the same run on the 32768-token history (K and V, all heads).
+
+Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "PQ decode-attn KV tokens/s & % HBM peak at 32K ctx; pq_encode tokens/s"
+HBM_PEAK_GBS = 8000.0
+# fp32 vector peak of MI355X: 256 CUs x 2.4 GHz x 128 lanes x 2 flops (packed FMA)
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama2_7b_32k")
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--encode-reps", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work for the baseline sample")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, r_len):
+    """Bytes the method itself must move for one decode call (per-unit figures)."""
+    M = w.n_sub
+    T = sum(w.hist_len)
+    codes = 2 * M * T * w.n_kv_heads                       # K and V codes, 2*M per history token per kv head
+    recent = 2 * 2 * w.head_dim * r_len * w.batch * w.n_kv_heads  # fp16 K and V
+    books = 2 * w.n_kv_heads * w.n_centroids * w.head_dim * 4      # fp32 K and V codebooks
+    q = 2 * w.head_dim * w.batch * w.n_q_heads
+    out = (4 * w.head_dim + 4) * w.batch * w.n_q_heads
+    return codes + recent + books + q + out
+
+
+def encode_bytes(w, n_tokens):
+    """fp16 K and V read, uint8 codes written, fp32 codebooks read, per encode of n_tokens per tensor."""
+    return 2 * (n_tokens * w.n_kv_heads * (2 * w.head_dim + w.n_sub) + w.n_kv_heads * w.n_centroids * w.head_dim * 4)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU leg.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_attention_pq_amd as P
+    import synthkv
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = synthkv.WORKLOADS[args.workload]
+    dev = "cuda"
+    B, Hq, Hkv, d, M = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_sub
+    T, R = w.max_hist, w.recent_len
+    t_cap = w.t_cap
+    dims = P.Dims(d, w.d_sub, w.n_centroids, Hq, Hkv)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+
+    # ---- inputs (single sequence per workload row of this bench)
+    t0 = time.time()
+    cbk = torch.from_numpy(synthkv.drawn_codebook(w, 0, "k")).to(dev)
+    cbv = torch.from_numpy(synthkv.drawn_codebook(w, 0, "v")).to(dev)
+    planes = {}
+    enc_ms = {}
+    for tensor, cb in (("k", cbk), ("v", cbv)):
+        x = torch.stack([torch.from_numpy(synthkv.history_kv(w, 0, tensor, b)) for b in range(B)]).to(dev)
+        codes = torch.zeros((B, Hkv, t_cap * M), dtype=torch.uint8, device=dev)
+        P.encode(dims, x, cb, codes, t_cap)  # warm-up and the codes used below
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.encode_reps):
+            P.encode(dims, x, cb, codes, t_cap)
+        e1.record()
+        torch.cuda.synchronize()
+        enc_ms[tensor] = e0.elapsed_time(e1) / args.encode_reps
+        planes[tensor] = codes
+        del x
+    print(f"[bench] inputs + encode ready in {time.time() - t0:.1f}s; encode K {enc_ms['k']:.3f} ms, "
+          f"V {enc_ms['v']:.3f} ms", file=sys.stderr, flush=True)
+
+    q = torch.from_numpy(synthkv.queries(w)).to(dev)
+    rk = torch.from_numpy(synthkv.recent_kv(w, 0, "k")).to(dev)
+    rv = torch.from_numpy(synthkv.recent_kv(w, 0, "v")).to(dev)
+    hist_len = torch.tensor(w.hist_len, dtype=torch.int32, device=dev)
+    recent_len = torch.full((B,), R, dtype=torch.int32, device=dev)
+
+    copies = []
+    for i in range(args.copies):
+        copies.append(dict(q=q.clone(), ck=planes["k"].clone(), cv=planes["v"].clone(), rk=rk.clone(),
+                           rv=rv.clone()))
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws_bytes = P.decode_workspace_bytes(dims, B, T)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        c = copies[i % len(copies)]
+        P.decode_attention(dims, c["q"], cbk, cbv, c["ck"], c["cv"], t_cap, hist_len, T, c["rk"], c["rv"],
+                           recent_len, scale, out, lse, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all(), "non-finite decode output"
+
+    kv_tokens = w.n_layers * (sum(w.hist_len) + B * R)
+    value = kv_tokens / (ms * 1e-3)
+    abytes = algorithmic_bytes(w, R)
+    achieved = abytes / (ms * 1e-3) / 1e9
+
+    enc_tokens = B * T * 2  # K and V tensors of every history token
+    enc_total_ms = enc_ms["k"] + enc_ms["v"]
+    enc_tok_s = enc_tokens / (enc_total_ms * 1e-3)
+    # brute-force encode work: per (token, head, subspace, centroid) d_sub subtractions and d_sub FMAs
+    enc_flops = enc_tokens * Hkv * M * w.n_centroids * (2 * w.d_sub)
+    enc_tflops = enc_flops / (enc_total_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "d_sub": w.d_sub, "centroids": w.n_centroids, "hist_tokens": T, "recent_tokens": R,
+                   "codes": "u8", "kv_dtype": w.dtype, "rotating_copies": args.copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pqkv_decode_attention call (history kernel + finalize kernel)",
+                     "algorithmic_bytes_per_call": abytes},
+        "encode": {"tokens_per_s": round(enc_tok_s, 1), "ms": round(enc_total_ms, 4),
+                   "tokens": enc_tokens, "bound": "alu", "achieved_tflops": round(enc_tflops, 2),
+                   "peak_tflops": FP32_VALU_PEAK_TFLOPS, "frac": round(enc_tflops / FP32_VALU_PEAK_TFLOPS, 4),
+                   "hbm_gbs": round(encode_bytes(w, B * T) / (enc_total_ms * 1e-3) / 1e9, 1)},
+    }
+    for c in copies:
+        c.clear()
+    torch.cuda.synchronize()
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, target_s):
+    """The CPU oracle (fp64 dequantise-then-exact attention) on a sample of the same workload:
+    the first few kv heads of the 32K layer, with seeded random codes.  Scaled to the
+    whole call by the head count."""
+    import oracle
+    import synthkv
+
+    d, M, K = w.head_dim, w.n_sub, w.n_centroids
+    T, R = w.max_hist, w.recent_len
+    h_s = 4
+    rng_q = synthkv.queries(w)[:, :h_s]
+    cbk = synthkv.drawn_codebook(w, 0, "k")[:h_s]
+    cbv = synthkv.drawn_codebook(w, 0, "v")[:h_s]
+    ck = synthkv.small_codes(7, (1, h_s, T, M), K)
+    cv = synthkv.small_codes(8, (1, h_s, T, M), K)
+    rk = synthkv.recent_kv(w, 0, "k")[:, :h_s]
+    rv = synthkv.recent_kv(w, 0, "v")[:, :h_s]
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    t0 = time.time()
+    reps = 0
+    while True:
+        oracle.decode_exact(rng_q, cbk, cbv, ck, cv, [T], rk, rv, [R], scale)
+        reps += 1
+        if time.time() - t0 >= target_s:
+            break
+    el = time.time() - t0
+    per_call = el / reps * (w.n_q_heads / h_s)
+    return {"value": round((T + R) / per_call, 1), "unit": "KV tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} x fp64 dequantise-then-exact attention over {h_s} of {w.n_q_heads} heads "
+                      f"({T}+{R} tokens), scaled to all heads; {el:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

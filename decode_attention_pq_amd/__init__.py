@@ -1,0 +1,182 @@
+"""Python binding of libpqkv: product-quantised KV cache (MILLION) on MI355X.
+
+Thin ctypes marshalling over the C interface declared in ``include/pqkv.h``:
+every call checks tensor shapes, dtypes and devices, passes raw device
+pointers and torch's current HIP stream, and turns a non-zero status into a
+``PQKVError``.  All computation runs in the HIP kernels of ``libpqkv.so``;
+there is no fallback path.  PyTorch only provides device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime libpqkv.so binds to (same soname)
+
+__all__ = [
+    "PQKVError", "Dims", "lib", "LIB_PATH", "encode", "build_lut", "decode_workspace_bytes",
+    "decode_attention", "merge", "code_plane_bytes", "F16", "F32", "MAX_RECENT", "TILE_TOKENS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpqkv.so")
+F16, F32 = 0, 1
+MAX_RECENT = 1024
+TILE_TOKENS = 64
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace missing or too small",
+           4: "HIP launch failed"}
+
+
+class PQKVError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {_STATUS.get(status, 'unknown')} (status {status})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("d_sub", ctypes.c_int32), ("n_centroids", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32)]
+
+    @property
+    def n_sub(self) -> int:
+        return self.head_dim // self.d_sub
+
+    def __repr__(self):
+        return (f"Dims(head_dim={self.head_dim}, d_sub={self.d_sub}, n_centroids={self.n_centroids}, "
+                f"n_q_heads={self.n_q_heads}, n_kv_heads={self.n_kv_heads})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpqkv.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libpqkv.so not built at {LIB_PATH}; run decode_attention_pq_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        dp = ctypes.POINTER(Dims)
+        L.pqkv_encode.argtypes = [dp, vp, i32, i32, i64, i64, i64, i64, vp, vp, i64, i64, vp]
+        L.pqkv_encode.restype = i32
+        L.pqkv_build_lut.argtypes = [dp, i32, vp, i32, vp, vp, vp]
+        L.pqkv_build_lut.restype = i32
+        L.pqkv_decode_workspace_bytes.argtypes = [dp, i32, i64]
+        L.pqkv_decode_workspace_bytes.restype = sz
+        L.pqkv_decode_attention.argtypes = [dp, i32, vp, i32, vp, vp, vp, vp, i64, vp, i64, vp, vp, i32, i64,
+                                            vp, f32, vp, vp, vp, sz, vp]
+        L.pqkv_decode_attention.restype = i32
+        L.pqkv_merge.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.pqkv_merge.restype = i32
+        L.pqkv_status_str.argtypes = [i32]
+        L.pqkv_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PQKVError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"expected float16 or float32, got {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libpqkv takes device tensors")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def code_plane_bytes(dims: Dims, t_cap: int) -> int:
+    return t_cap * dims.n_sub
+
+
+def encode(dims: Dims, x: torch.Tensor, codebook: torch.Tensor, codes: torch.Tensor, t_cap: int,
+           t_start: int = 0) -> None:
+    """pqkv_encode.  x: [n_seqs, n_tokens, Hkv, d] or [n_tokens, Hkv, d] (last dim contiguous);
+    codebook: fp32 [Hkv, K, M, d_sub]; codes: uint8 [n_seqs, Hkv, t_cap*M] (or [Hkv, t_cap*M])."""
+    _dev(x, codebook, codes)
+    if x.dim() == 3:
+        x = x.unsqueeze(0)
+    n_seqs, n_tok, H, d = x.shape
+    if x.stride(3) != 1:
+        raise ValueError("x rows must be contiguous")
+    if codebook.dtype != torch.float32 or not codebook.is_contiguous():
+        raise ValueError("codebook must be contiguous fp32")
+    if codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError("codes must be contiguous uint8")
+    if codes.numel() < n_seqs * dims.n_kv_heads * t_cap * dims.n_sub:
+        raise ValueError("codes buffer too small")
+    _check("pqkv_encode", lib().pqkv_encode(
+        ctypes.byref(dims), _ptr(x), _dtype_code(x), n_seqs, n_tok, x.stride(0), x.stride(1), x.stride(2),
+        _ptr(codebook), _ptr(codes), t_cap, t_start, _stream()))
+
+
+def build_lut(dims: Dims, q: torch.Tensor, codebook_k: torch.Tensor, lut: torch.Tensor) -> None:
+    """pqkv_build_lut.  q: [B, Hq, d] contiguous; lut: fp32 [B, Hq, M, K]."""
+    _dev(q, codebook_k, lut)
+    if not q.is_contiguous() or not lut.is_contiguous() or lut.dtype != torch.float32:
+        raise ValueError("q and lut must be contiguous; lut fp32")
+    B = q.shape[0]
+    if lut.numel() < B * dims.n_q_heads * dims.n_sub * dims.n_centroids:
+        raise ValueError("lut buffer too small")
+    _check("pqkv_build_lut", lib().pqkv_build_lut(ctypes.byref(dims), B, _ptr(q), _dtype_code(q),
+                                                  _ptr(codebook_k), _ptr(lut), _stream()))
+
+
+def decode_workspace_bytes(dims: Dims, batch: int, max_hist_len: int) -> int:
+    return int(lib().pqkv_decode_workspace_bytes(ctypes.byref(dims), batch, max_hist_len))
+
+
+def decode_attention(dims: Dims, q, codebook_k, codebook_v, codes_k, codes_v, t_cap: int, hist_len,
+                     max_hist_len: int, recent_k, recent_v, recent_len, softmax_scale: float, out, lse,
+                     workspace) -> None:
+    """pqkv_decode_attention.  q: [B, Hq, d]; codes_k/v: uint8 [B, Hkv, t_cap*M];
+    hist_len/recent_len: int32 [B] (device); recent_k/v: [B, Hkv, r_cap, d] or None;
+    out: fp32 [B, Hq, d]; lse: fp32 [B, Hq]; workspace: a device tensor (uint8) or None."""
+    _dev(q, codebook_k, codebook_v, codes_k, codes_v, hist_len, recent_k, recent_v, recent_len, out, lse,
+         workspace)
+    B = q.shape[0]
+    for t in (q, codebook_k, codebook_v, codes_k, codes_v, out, lse):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if hist_len.dtype != torch.int32:
+        raise ValueError("hist_len must be int32")
+    r_cap = 0 if recent_k is None else recent_k.shape[2]
+    rdt = F16 if recent_k is None else _dtype_code(recent_k)
+    if recent_k is not None:
+        if not (recent_k.is_contiguous() and recent_v.is_contiguous()) or recent_len.dtype != torch.int32:
+            raise ValueError("recent_k/v must be contiguous and recent_len int32")
+        if recent_k.shape != recent_v.shape or recent_k.dtype != recent_v.dtype:
+            raise ValueError("recent_k and recent_v differ")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pqkv_decode_attention", lib().pqkv_decode_attention(
+        ctypes.byref(dims), B, _ptr(q), _dtype_code(q), _ptr(codebook_k), _ptr(codebook_v), _ptr(codes_k),
+        _ptr(codes_v), t_cap, _ptr(hist_len), max_hist_len, _ptr(recent_k), _ptr(recent_v), rdt, r_cap,
+        _ptr(recent_len), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream()))
+
+
+def merge(out_a, lse_a, out_b, lse_b, out, lse) -> None:
+    """pqkv_merge over rows: out_*: fp32 [n, d]; lse_*: fp32 [n]."""
+    _dev(out_a, lse_a, out_b, lse_b, out, lse)
+    n, d = out_a.shape[0], out_a.shape[-1]
+    for t in (out_a, lse_a, out_b, lse_b, out, lse):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("merge takes contiguous fp32 tensors")
+    _check("pqkv_merge", lib().pqkv_merge(n, d, _ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out),
+                                          _ptr(lse), _stream()))

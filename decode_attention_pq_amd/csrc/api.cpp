@@ -1,0 +1,201 @@
+// libpqkv C interface: argument validation, split planning and dispatch.
+//
+// Every entry point validates its arguments on the host and returns a status
+// before anything is enqueued; kernels are launched asynchronously on the
+// caller's stream.  No exception crosses the interface.
+
+#include <cstdint>
+#include <cstring>
+
+#include "pqkv_internal.h"
+
+namespace pqkv {
+namespace {
+
+bool dims_ok(const pqkv_dims* d) {
+    if (!d) return false;
+    if (d->head_dim != 64 && d->head_dim != 128) return false;
+    if (d->d_sub != 2 && d->d_sub != 4) return false;
+    if (d->n_centroids < 2 || d->n_centroids > 256) return false;
+    if (d->n_q_heads < 1 || d->n_kv_heads < 1) return false;
+    if (d->n_q_heads % d->n_kv_heads) return false;
+    if (d->n_kv_heads > 65535) return false;
+    return true;
+}
+
+bool dtype_ok(pqkv_dtype t) { return t == PQKV_F16 || t == PQKV_F32; }
+
+size_t dtype_bytes(pqkv_dtype t) { return t == PQKV_F16 ? 2 : 4; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Distinguish "bad argument" from "well-formed but not supported".
+pqkv_status check_dims(const pqkv_dims* d) {
+    if (!d) return PQKV_ERR_INVALID;
+    if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 || d->d_sub < 1 || d->n_centroids < 1)
+        return PQKV_ERR_INVALID;
+    if (d->n_q_heads % d->n_kv_heads || d->head_dim % d->d_sub) return PQKV_ERR_INVALID;
+    return dims_ok(d) ? PQKV_OK : PQKV_ERR_UNSUPPORTED;
+}
+
+pqkv_status hip_status(hipError_t e) { return e == hipSuccess ? PQKV_OK : PQKV_ERR_HIP; }
+
+}  // namespace
+
+DecodePlan plan_decode(const pqkv_dims& d, int32_t batch, int64_t max_hist_len) {
+    DecodePlan p{};
+    const int M = d.head_dim / d.d_sub;
+    const int g = d.n_q_heads / d.n_kv_heads;
+    // query heads per work-group: as many as share an LDS row, dividing the group size
+    int qh = 1;
+    for (int c : {4, 2}) {
+        if (c * M <= 64 && g % c == 0) {
+            qh = c;
+            break;
+        }
+    }
+    p.qh = qh;
+    p.n_groups = g / qh;
+    p.partial_stride = d.head_dim + 4;
+    p.units = (int64_t)batch * d.n_kv_heads * p.n_groups;
+    if (max_hist_len <= 0) {
+        // recent window only: one work-group per unit
+        p.rounds = 0;
+        p.n_split = 1;
+        p.split_tokens = 0;
+    } else {
+        const int max_rounds = decode_max_rounds(M, qh);
+        // enough splits to give every compute unit a work-group, then as few
+        // rounds per wave as that allows
+        int64_t n_split = (kPlanCUs + p.units - 1) / p.units;
+        int64_t rounds = (max_hist_len + n_split * kTokensPerRound - 1) / (n_split * kTokensPerRound);
+        if (rounds < 1) rounds = 1;
+        if (rounds > max_rounds) rounds = max_rounds;
+        n_split = (max_hist_len + rounds * kTokensPerRound - 1) / (rounds * kTokensPerRound);
+        p.rounds = (int)rounds;
+        p.n_split = (int)n_split;
+        p.split_tokens = rounds * kTokensPerRound;
+    }
+    const size_t part = (size_t)batch * d.n_q_heads * p.n_split * p.partial_stride * sizeof(float);
+    p.counters_offset = (part + 255) / 256 * 256;
+    p.workspace_bytes = p.counters_offset + ((size_t)p.units * sizeof(uint32_t) + 255) / 256 * 256;
+    return p;
+}
+
+}  // namespace pqkv
+
+using namespace pqkv;
+
+extern "C" {
+
+const char* pqkv_status_str(pqkv_status s) {
+    switch (s) {
+        case PQKV_OK: return "ok";
+        case PQKV_ERR_INVALID: return "invalid argument";
+        case PQKV_ERR_UNSUPPORTED: return "unsupported shape";
+        case PQKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case PQKV_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+pqkv_status pqkv_encode(const pqkv_dims* dims, const void* x, pqkv_dtype x_dtype, int32_t n_seqs,
+                        int64_t n_tokens, int64_t x_seq_stride, int64_t x_tok_stride,
+                        int64_t x_head_stride, const float* codebook, uint8_t* codes, int64_t t_cap,
+                        int64_t t_start, hipStream_t stream) {
+    const pqkv_status ds = check_dims(dims);
+    if (ds != PQKV_OK) return ds;
+    if (!dtype_ok(x_dtype)) return PQKV_ERR_INVALID;
+    if (n_seqs < 0 || n_tokens < 0 || t_start < 0 || t_cap <= 0 || t_cap % kTileTokens) return PQKV_ERR_INVALID;
+    if (x_seq_stride < 0 || x_tok_stride < 0 || x_head_stride < 0) return PQKV_ERR_INVALID;
+    if (t_start + n_tokens > t_cap) return PQKV_ERR_INVALID;
+    if (n_seqs > 65535) return PQKV_ERR_UNSUPPORTED;
+    if (n_seqs == 0 || n_tokens == 0) return PQKV_OK;
+    if (!x || !codebook || !codes) return PQKV_ERR_INVALID;
+    // every row is read with 16-byte loads
+    const int64_t row_align = 16 / (int64_t)dtype_bytes(x_dtype);
+    if (!aligned(x, 16) || x_seq_stride % row_align || x_tok_stride % row_align || x_head_stride % row_align)
+        return PQKV_ERR_INVALID;
+    if (!aligned(codebook, 16)) return PQKV_ERR_INVALID;
+    if ((n_tokens + 511) / 512 > 0x7fffffffLL) return PQKV_ERR_UNSUPPORTED;
+    return hip_status(launch_encode(*dims, x, x_dtype, n_seqs, n_tokens, x_seq_stride, x_tok_stride,
+                                    x_head_stride, codebook, codes, t_cap, t_start, stream));
+}
+
+pqkv_status pqkv_build_lut(const pqkv_dims* dims, int32_t batch, const void* q, pqkv_dtype q_dtype,
+                           const float* codebook_k, float* lut, hipStream_t stream) {
+    const pqkv_status ds = check_dims(dims);
+    if (ds != PQKV_OK) return ds;
+    if (!dtype_ok(q_dtype) || batch < 0) return PQKV_ERR_INVALID;
+    if (batch == 0) return PQKV_OK;
+    if (!q || !codebook_k || !lut) return PQKV_ERR_INVALID;
+    if ((int64_t)batch * dims->n_q_heads > 0x7fffffffLL) return PQKV_ERR_UNSUPPORTED;
+    return hip_status(launch_build_lut(*dims, batch, q, q_dtype, codebook_k, lut, stream));
+}
+
+size_t pqkv_decode_workspace_bytes(const pqkv_dims* dims, int32_t batch, int64_t max_hist_len) {
+    if (check_dims(dims) != PQKV_OK || batch <= 0 || max_hist_len < 0) return 0;
+    return plan_decode(*dims, batch, max_hist_len).workspace_bytes;
+}
+
+pqkv_status pqkv_decode_attention(const pqkv_dims* dims, int32_t batch, const void* q,
+                                  pqkv_dtype q_dtype, const float* codebook_k,
+                                  const float* codebook_v, const uint8_t* codes_k,
+                                  const uint8_t* codes_v, int64_t t_cap, const int32_t* hist_len,
+                                  int64_t max_hist_len, const void* recent_k, const void* recent_v,
+                                  pqkv_dtype recent_dtype, int64_t r_cap,
+                                  const int32_t* recent_len, float softmax_scale, float* out,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    const pqkv_status ds = check_dims(dims);
+    if (ds != PQKV_OK) return ds;
+    if (!dtype_ok(q_dtype) || !dtype_ok(recent_dtype)) return PQKV_ERR_INVALID;
+    if (batch < 0 || max_hist_len < 0 || r_cap < 0 || t_cap < 0) return PQKV_ERR_INVALID;
+    if (max_hist_len > 0 && (t_cap % kTileTokens || max_hist_len > t_cap)) return PQKV_ERR_INVALID;
+    if (r_cap > PQKV_MAX_RECENT) return PQKV_ERR_UNSUPPORTED;
+    if (batch == 0) return PQKV_OK;
+    if (!q || !out || !lse) return PQKV_ERR_INVALID;
+    if (max_hist_len > 0) {
+        if (!codebook_k || !codebook_v || !codes_k || !codes_v || !hist_len) return PQKV_ERR_INVALID;
+        if (!aligned(codes_k, 16) || !aligned(codes_v, 16)) return PQKV_ERR_INVALID;
+    }
+    if (r_cap > 0 && (!recent_k || !recent_v || !recent_len)) return PQKV_ERR_INVALID;
+    if (!(softmax_scale == softmax_scale)) return PQKV_ERR_INVALID;  // NaN
+    if ((int64_t)batch * dims->n_q_heads > 0x7fffffffLL) return PQKV_ERR_UNSUPPORTED;
+    const DecodePlan plan = plan_decode(*dims, batch, max_hist_len);
+    if (plan.n_split > kMaxSplits || plan.units * plan.n_split > 0x7fffffffLL - 8) return PQKV_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned(workspace, 256)) return PQKV_ERR_WORKSPACE;
+
+    DecodeArgs a;
+    a.q = q;
+    a.cb_k = codebook_k;
+    a.cb_v = codebook_v;
+    a.codes_k = codes_k;
+    a.codes_v = codes_v;
+    a.t_cap = t_cap;
+    a.hist_len = hist_len;
+    a.max_hist = max_hist_len;
+    a.rk = r_cap > 0 ? recent_k : nullptr;
+    a.rv = r_cap > 0 ? recent_v : nullptr;
+    a.r_cap = r_cap;
+    a.recent_len = r_cap > 0 ? recent_len : nullptr;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.out = out;
+    a.lse = lse;
+    a.partials = static_cast<float*>(workspace);
+    a.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.counters_offset);
+    return hip_status(launch_decode(*dims, batch, q_dtype, recent_dtype, plan, a, stream));
+}
+
+pqkv_status pqkv_merge(int64_t n_rows, int32_t head_dim, const float* out_a, const float* lse_a,
+                       const float* out_b, const float* lse_b, float* out, float* lse,
+                       hipStream_t stream) {
+    if (n_rows < 0 || head_dim < 1) return PQKV_ERR_INVALID;
+    if (head_dim > 1024) return PQKV_ERR_UNSUPPORTED;
+    if (n_rows == 0) return PQKV_OK;
+    if (!out_a || !lse_a || !out_b || !lse_b || !out || !lse) return PQKV_ERR_INVALID;
+    if ((n_rows + 3) / 4 > 0x7fffffffLL) return PQKV_ERR_UNSUPPORTED;
+    return hip_status(launch_merge_states(n_rows, head_dim, out_a, lse_a, out_b, lse_b, out, lse, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,662 @@
+// PQ decode attention in one kernel: ad-LUT scoring of the compressed history,
+// split-over-tokens softmax with a per-subspace histogram value side, exact
+// attention over the recent full-precision window, and the log-sum-exp merge.
+//
+// MILLION write-up (DAC 2025), page "MILLION":
+//   - Fig. 7 paragraph: history attention and new-token attention are computed
+//     apart and combined; because the history is much longer than the codebook,
+//     the query x codebook asymmetric-distance table (ad-LUT) is built first and
+//     replaces per-token inner products.
+//   - Fig. 8 paragraph: a flash-decoding base (the history is split across
+//     work-groups and their partial softmax states are reduced) with packed codes
+//     loaded as wide words.
+//
+// gfx950 design (not the page's GPU design):
+//   - One work-group of 512 threads per (sequence, kv head, query-head group,
+//     history split).  Work-group ids are remapped so that all splits of one kv
+//     head run on the same XCD and share its L2 copy of the codebooks.
+//   - Every wave owns whole 64-token tiles; a lane holds one token's M codes,
+//     read with M/16 16-byte loads that are contiguous across the wave.  A wave
+//     walks one stream of tiles -- its K tiles, then the V tiles of the same
+//     tokens -- keeping three tiles in flight ahead of the one in use.  The
+//     codebook values for the LUT are requested before the first tiles, because
+//     vector-memory loads of a wave retire in issue order.
+//   - LDS holds the ad-LUT of the work-group's QH query heads (bytes 0..64K) and
+//     a u32 histogram of the same shape (bytes 64K..128K): row c = centroid c,
+//     entry j*M + m = (query head j, subspace m).  The code-cache layout rotates
+//     each token's bytes by its slot, so at every step the 64 lanes address 64
+//     different subspaces and the LDS accesses never conflict; one v_perm_b32
+//     per code forms the byte address (code << 8) | (4*m), plus 0x10000 for the
+//     histogram.
+//   - Two-phase softmax inside the work-group: scores stay in registers, the
+//     work-group max is taken once, then p = exp2(s - max) is added into the
+//     histogram.  The adds are u32 fixed point (round(p * 2^S)): on gfx950 an
+//     fp32 LDS add serialises the wave (~190 clk per instruction) while the u32
+//     add takes ~4 clk.  S is chosen so that no histogram cell can overflow.
+//   - Each work-group also takes a slice of the recent window (exact fp32 dot
+//     products), writes its partial (max, sum, unnormalised output), and the
+//     last work-group of a (sequence, kv head, group) to finish merges all
+//     partials into out and lse (completion counter in the workspace).
+
+#include <hip/hip_fp16.h>
+
+#include "pqkv_internal.h"
+
+namespace pqkv {
+namespace {
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kThreads = kDecodeThreads;
+constexpr int kWaves = kDecodeWaves;
+constexpr int kRow = 64;  // floats per LDS table row
+constexpr int kPrefetch = 3;  // code tiles a wave keeps in flight ahead of use
+constexpr int kRecentPre = 4; // recent rows per wave requested before the first tiles
+
+__device__ inline float to_f32(float v) { return v; }
+__device__ inline float to_f32(__half v) { return __half2float(v); }
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ inline uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Histogram byte address of byte s of code word `cw`, with byte s of offset word
+// `mw`: (code << 8) | (4*m).  v_perm_b32 selector: result byte 0 = source-1 byte
+// s, byte 1 = source-0 byte s, bytes 2 and 3 = 0.
+template <int S>
+__device__ inline uint32_t hist_addr(uint32_t cw, uint32_t mw) {
+    constexpr uint32_t sel = 0x0c0c0000u | ((4u + S) << 8) | (uint32_t)S;
+    return __builtin_amdgcn_perm(cw, mw, sel);
+}
+
+// Same for the LUT at LDS byte 65536: `ml` holds the offsets of two steps in
+// bytes 0-1 and the constant 1 in byte 2, giving 0x10000 | (code << 8) | (4*m).
+template <int S>
+__device__ inline uint32_t lut_addr(uint32_t cw, uint32_t ml) {
+    constexpr uint32_t sel = 0x0c000000u | (2u << 16) | ((4u + S) << 8) | (uint32_t)(S & 1);
+    return __builtin_amdgcn_perm(cw, ml, sel);
+}
+
+__device__ inline float lds_f32(const float* base, uint32_t byte_off) {
+    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+__device__ inline void lds_add_u32(float* base, uint32_t byte_off, uint32_t v) {
+    __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(base) + byte_off), v,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Read by loads whose slot is unused (a tile past the history, a missing
+// codebook): every prefetch is issued unconditionally, which lets the compiler
+// count outstanding loads exactly instead of waiting for all of them.
+__device__ uint4 g_zero_block[kTileTokens * 4];
+
+// Cross-work-group partial results: device-coherent store and load.
+__device__ inline void publish(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline float collect(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int NCH>
+__device__ inline void load_tile(uint4 (&cw)[NCH], const uint8_t* __restrict__ plane, int64_t tile, int lane,
+                                 bool ok) {
+    const uint8_t* p = ok ? plane + tile * (kTileTokens * NCH * 16) : reinterpret_cast<const uint8_t*>(g_zero_block);
+    p += lane * 16;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) cw[c] = *reinterpret_cast<const uint4*>(p + c * (kTileTokens * 16));
+}
+
+struct DecArgs {
+    const void* q;
+    const float* cb_k;
+    const float* cb_v;
+    const uint8_t* codes_k;
+    const uint8_t* codes_v;
+    int64_t t_cap;
+    const int32_t* hist_len;
+    int64_t max_hist;
+    const void* rk;
+    const void* rv;
+    int64_t r_cap;
+    const int32_t* recent_len;
+    float scale_log2;
+    float fix_scale;  // 2^S
+    float fix_inv;    // 2^-S
+    float* partials;
+    uint32_t* counters;
+    float* out;
+    float* lse;
+    int K, Hq, Hkv, n_groups, n_split, rounds, pstride, n_items, per_xcd;
+    int64_t split_tokens;
+};
+
+template <int M, int DSUB, int QH, typename QT, typename RT>
+__global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
+    constexpr int D = M * DSUB;
+    constexpr int NCH = M / 16;
+    constexpr int RW = decode_max_rounds(M, QH);
+    constexpr int RS = PQKV_MAX_RECENT;
+    constexpr int P = kPrefetch;          // tiles in flight ahead of the one being used
+    constexpr int NSLOT = P + 1;
+    constexpr int LUT_PER_THREAD = kLdsRows * M / kThreads;  // (centroid, subspace) pairs per thread
+    constexpr int CPL = D / 64;                // epilogue: output components per lane
+    constexpr int CPER = kLdsRows / kWaves;    // epilogue: centroids per wave
+    static_assert(QH * M <= kRow, "query-head group must fit one LDS row");
+    static_assert(2 * kMaxSplits <= RS, "the merge keeps split maxima and sums in rs");
+
+    // LDS: histogram (u32) at byte 0, LUT at byte 65536, then the small buffers.
+    __shared__ float lds[2 * kLdsRows * kRow];
+    __shared__ float ored[kWaves * QH * D];     // per-wave output partials
+    __shared__ float qs[QH * D];                // query * scale * log2(e)
+    __shared__ float rs[QH * RS];               // recent scores, then weights * 2^S
+    __shared__ float red[kWaves * QH];
+    __shared__ uint32_t redu[kWaves * QH];
+    __shared__ int last_flag;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(lds);
+    float* table = lds + kLdsRows * kRow;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    // XCD-aware work mapping: ids that share an XCD (id mod 8) get contiguous items
+    const int L = blockIdx.x;
+    const int item = (L & 7) * a.per_xcd + (L >> 3);
+    if (item >= a.n_items) return;
+    const int unit = item / a.n_split;
+    const int split = item - unit * a.n_split;
+    const int grp = unit % a.n_groups;
+    const int bh = unit / a.n_groups;
+    const int h = bh % a.Hkv;
+    const int b = bh / a.Hkv;
+    const int hq0 = h * (a.Hq / a.Hkv) + grp * QH;
+    const int K = a.K;
+
+    int64_t T = a.hist_len[b];
+    T = T < 0 ? 0 : (T > a.max_hist ? a.max_hist : T);
+    const int64_t t0 = (int64_t)split * a.split_tokens;
+    const int64_t t1 = T < t0 + a.split_tokens ? T : t0 + a.split_tokens;
+    int R = a.recent_len ? a.recent_len[b] : 0;
+    R = R < 0 ? 0 : (R > a.r_cap ? (int)a.r_cap : R);
+    const int rs_per = (R + a.n_split - 1) / a.n_split;
+    const int r0 = split * rs_per;
+    const int n_rec = R - r0 < rs_per ? (R - r0 > 0 ? R - r0 : 0) : rs_per;
+    const bool has_hist = t0 < t1;
+    const int64_t tile0 = t0 / kTileTokens;
+    const int rounds = a.rounds;
+
+    const int64_t plane_off = ((int64_t)b * a.Hkv + h) * a.t_cap * M;
+    const uint8_t* plane_k = a.codes_k + plane_off;
+    const uint8_t* plane_v = a.codes_v + plane_off;
+
+    // Step s < RW scores K tile s of this wave; step RW + s adds V tile s into the
+    // histogram.  Tile of round r: tile0 + r*8 + wave.
+    auto step_tile = [&](int s) -> int64_t { return tile0 + (int64_t)(s < RW ? s : s - RW) * kWaves + wave; };
+    auto step_ok = [&](int s) -> bool {
+        const int r = s < RW ? s : s - RW;
+        return r < rounds && step_tile(s) * kTileTokens < t1;
+    };
+    auto issue = [&](uint4 (&slot)[NCH], int s) {
+        load_tile<NCH>(slot, s < RW ? plane_k : plane_v, step_tile(s), lane, step_ok(s));
+    };
+
+    // ---- 1. loads in the order they are needed (a wave's loads retire in issue
+    //         order): query, the first recent rows, codebook values, first tiles
+    const QT* qrow = static_cast<const QT*>(a.q) + (int64_t)(b * a.Hq + hq0) * D;
+    const float qval = to_f32(qrow[tid < QH * D ? tid : 0]) * a.scale_log2;
+    const RT* rk = static_cast<const RT*>(a.rk) + (((int64_t)b * a.Hkv + h) * a.r_cap + r0) * D;
+    const RT* rv = static_cast<const RT*>(a.rv) + (((int64_t)b * a.Hkv + h) * a.r_cap + r0) * D;
+    const RT* rzero = reinterpret_cast<const RT*>(g_zero_block);
+    float kpre[kRecentPre][D / 64];
+#pragma unroll
+    for (int p = 0; p < kRecentPre; ++p) {
+        const int i = wave + p * kWaves;
+        const RT* row = i < n_rec ? rk + (int64_t)i * D + lane : rzero;
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) kpre[p][k] = to_f32(row[i < n_rec ? 64 * k : 0]);
+    }
+    float cbv_reg[LUT_PER_THREAD][DSUB];
+    const float* cbh = a.cb_k ? a.cb_k + (int64_t)h * K * M * DSUB : reinterpret_cast<const float*>(g_zero_block);
+    const int cstride = a.cb_k ? M * DSUB : 0;
+#pragma unroll
+    for (int k = 0; k < LUT_PER_THREAD; ++k) {
+        const int e = tid + k * kThreads;
+        int c = e / M;
+        const int m = a.cb_k ? e - c * M : 0;
+        c = c < K ? c : K - 1;
+        const float* cc = cbh + (int64_t)c * cstride + m * DSUB;
+#pragma unroll
+        for (int i = 0; i < DSUB; ++i) cbv_reg[k][i] = cc[i];
+    }
+    uint4 ring[NSLOT][NCH];
+#pragma unroll
+    for (int s = 0; s < P; ++s) issue(ring[s], s);
+    if (tid < QH * D) qs[tid] = qval;
+    __syncthreads();
+
+    // ---- 2. ad-LUT in LDS, recent-window scores, per-lane subspace offsets
+    if (has_hist) {
+#pragma unroll
+        for (int k = 0; k < LUT_PER_THREAD; ++k) {
+            const int e = tid + k * kThreads;
+            const int c = e / M;
+            const int m = e - c * M;
+            if (c < K) {
+#pragma unroll
+                for (int j = 0; j < QH; ++j) {
+                    const float* qq = qs + j * D + m * DSUB;
+                    float s = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < DSUB; ++i) s = fmaf(qq[i], cbv_reg[k][i], s);
+                    table[c * kRow + j * M + m] = s;
+                }
+            }
+        }
+    }
+    for (int i = wave, p = 0; i < n_rec; i += kWaves, ++p) {
+        float kv[D / 64];
+        if (p < kRecentPre) {  // prefetched above
+#pragma unroll
+            for (int q = 0; q < kRecentPre; ++q)
+                if (q == p)
+#pragma unroll
+                    for (int k = 0; k < D / 64; ++k) kv[k] = kpre[q][k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < D / 64; ++k) kv[k] = to_f32(rk[(int64_t)i * D + lane + 64 * k]);
+        }
+#pragma unroll
+        for (int j = 0; j < QH; ++j) {
+            float s = 0.0f;
+#pragma unroll
+            for (int k = 0; k < D / 64; ++k) s = fmaf(qs[j * D + lane + 64 * k], kv[k], s);
+            s = wave_sum(s);
+            if (lane == 0) rs[j * RS + i] = s;
+        }
+    }
+    // ml[k]: subspace byte offsets 4*((2k + slot) mod M) and 4*((2k + 1 + slot) mod M)
+    // in bytes 0-1 and the LUT's 64 KiB base in byte 2
+    uint32_t ml[M / 2];
+#pragma unroll
+    for (int k = 0; k < M / 2; ++k)
+        ml[k] = 0x10000u | (uint32_t)(((2 * k + lane) & (M - 1)) * 4) |
+                ((uint32_t)(((2 * k + 1 + lane) & (M - 1)) * 4) << 8);
+    __syncthreads();
+
+    // ---- 3. phase 1: K codes -> scores (log2 domain)
+    float sc[RW][QH];
+#pragma unroll
+    for (int s = 0; s < RW; ++s) {
+        issue(ring[(s + P) % NSLOT], s + P);
+#pragma unroll
+        for (int j = 0; j < QH; ++j) sc[s][j] = -INFINITY;
+        if (step_ok(s)) {
+            const uint4(&cw)[NCH] = ring[s % NSLOT];
+            float acc[QH][4];
+#pragma unroll
+            for (int j = 0; j < QH; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[j][t] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const uint32_t words[4] = {cw[c].x, cw[c].y, cw[c].z, cw[c].w};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t a0 = lut_addr<0>(words[w], ml[c * 8 + 2 * w]);
+                    const uint32_t a1 = lut_addr<1>(words[w], ml[c * 8 + 2 * w]);
+                    const uint32_t a2 = lut_addr<2>(words[w], ml[c * 8 + 2 * w + 1]);
+                    const uint32_t a3 = lut_addr<3>(words[w], ml[c * 8 + 2 * w + 1]);
+#pragma unroll
+                    for (int j = 0; j < QH; ++j) {
+                        const float* lj = lds + j * M;  // addresses carry the 65536 base
+                        acc[j][0] += lds_f32(lj, a0);
+                        acc[j][1] += lds_f32(lj, a1);
+                        acc[j][2] += lds_f32(lj, a2);
+                        acc[j][3] += lds_f32(lj, a3);
+                    }
+                }
+            }
+            const bool tok_ok = step_tile(s) * kTileTokens + lane < t1;
+#pragma unroll
+            for (int j = 0; j < QH; ++j)
+                sc[s][j] = tok_ok ? (acc[j][0] + acc[j][1]) + (acc[j][2] + acc[j][3]) : -INFINITY;
+        }
+    }
+
+    // zero the histogram (its region is not touched before phase 2)
+    if (has_hist)
+        for (int e = tid; e < K * kRow / 4; e += kThreads)
+            reinterpret_cast<uint4*>(hist)[e] = make_uint4(0u, 0u, 0u, 0u);
+
+    // ---- 4. work-group max over history and recent scores
+#pragma unroll
+    for (int j = 0; j < QH; ++j) {
+        float v = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < RW; ++s) v = fmaxf(v, sc[s][j]);
+        for (int i = tid; i < n_rec; i += kThreads) v = fmaxf(v, rs[j * RS + i]);
+        v = wave_max(v);
+        if (lane == 0) red[wave * QH + j] = v;
+    }
+    __syncthreads();
+    float mx[QH];
+#pragma unroll
+    for (int j = 0; j < QH; ++j) {
+        float v = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v = fmaxf(v, red[w * QH + j]);
+        mx[j] = v;
+    }
+    const bool any = mx[0] != -INFINITY;  // the split holds at least one token (all heads alike)
+
+    // ---- 5. phase 2: add round(p * 2^S) into histogram[code][m].
+    // First request this thread's value-codebook entries for the epilogue: lane
+    // (cg, m) of wave w covers subspace m, components [cg*CPL, cg*CPL + CPL) and
+    // centroids [w*CPER, w*CPER + CPER).
+    const int em = lane % M;
+    const int ecomp = (lane / M) * CPL;
+    const int ec0 = wave * CPER;
+    const float* cbv = a.cb_v ? a.cb_v + (int64_t)h * K * M * DSUB + em * DSUB + ecomp
+                              : reinterpret_cast<const float*>(g_zero_block);
+    const int vstride = a.cb_v ? M * DSUB : 0;
+    float cvr[CPER][CPL];
+#pragma unroll
+    for (int k = 0; k < CPER; ++k) {
+        const int c = ec0 + k < K ? ec0 + k : K - 1;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) cvr[k][i] = cbv[(int64_t)c * vstride + i];
+    }
+    float vpre[kRecentPre][CPL];  // recent value rows of this wave's first recent tokens
+#pragma unroll
+    for (int p = 0; p < kRecentPre; ++p) {
+        const int i = wave + p * kWaves;
+        const RT* row = i < n_rec ? rv + (int64_t)i * D + em * DSUB + ecomp : rzero;
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) vpre[p][t] = to_f32(row[i < n_rec ? t : 0]);
+    }
+    // byte s of mw[k] = 4 * ((4k + s + slot) mod M): subspace byte offsets
+    uint32_t mw[M / 4];
+#pragma unroll
+    for (int k = 0; k < M / 4; ++k) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) w |= (uint32_t)(((4 * k + s + lane) & (M - 1)) * 4) << (8 * s);
+        mw[k] = w;
+    }
+    uint32_t lsum[QH];
+#pragma unroll
+    for (int j = 0; j < QH; ++j) lsum[j] = 0u;
+#pragma unroll
+    for (int s = RW; s < 2 * RW; ++s) {
+        issue(ring[(s + P) % NSLOT], s + P);
+        if (step_ok(s) && step_tile(s) * kTileTokens + lane < t1) {
+            const uint4(&cw)[NCH] = ring[s % NSLOT];
+            uint32_t p[QH];
+#pragma unroll
+            for (int j = 0; j < QH; ++j) {
+                p[j] = __float2uint_rn(exp2f(sc[s - RW][j] - mx[j]) * a.fix_scale);
+                lsum[j] += p[j];
+            }
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const uint32_t words[4] = {cw[c].x, cw[c].y, cw[c].z, cw[c].w};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t mwv = mw[c * 4 + w];
+                    const uint32_t a0 = hist_addr<0>(words[w], mwv);
+                    const uint32_t a1 = hist_addr<1>(words[w], mwv);
+                    const uint32_t a2 = hist_addr<2>(words[w], mwv);
+                    const uint32_t a3 = hist_addr<3>(words[w], mwv);
+#pragma unroll
+                    for (int j = 0; j < QH; ++j) {
+                        float* hj = lds + j * M;
+                        lds_add_u32(hj, a0, p[j]);
+                        lds_add_u32(hj, a1, p[j]);
+                        lds_add_u32(hj, a2, p[j]);
+                        lds_add_u32(hj, a3, p[j]);
+                    }
+                }
+            }
+        }
+    }
+    // recent weights, scaled by 2^S like the histogram
+#pragma unroll
+    for (int j = 0; j < QH; ++j) {
+        float l = 0.0f;
+        for (int i = tid; i < n_rec; i += kThreads) {
+            const float p = exp2f(rs[j * RS + i] - mx[j]) * a.fix_scale;
+            rs[j * RS + i] = p;
+            l += p;
+        }
+        l = wave_sum(l);
+        const uint32_t lh = wave_sum_u32(lsum[j]);
+        if (lane == 0) {
+            red[wave * QH + j] = l;
+            redu[wave * QH + j] = lh;
+        }
+    }
+    __syncthreads();
+
+    // ---- 6. output partial: histogram x value codebook + recent weights x values
+    float* part = a.partials + ((int64_t)(b * a.Hq + hq0) * a.n_split + split) * a.pstride;
+    const int64_t head_step = (int64_t)a.n_split * a.pstride;
+    {
+        float acc[QH][CPL];
+#pragma unroll
+        for (int j = 0; j < QH; ++j)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) acc[j][i] = 0.0f;
+        if (any) {
+            if (has_hist) {
+#pragma unroll
+                for (int k = 0; k < CPER; ++k) {
+                    if (ec0 + k < K) {
+#pragma unroll
+                        for (int j = 0; j < QH; ++j) {
+                            const float hv = (float)hist[(ec0 + k) * kRow + j * M + em];
+#pragma unroll
+                            for (int i = 0; i < CPL; ++i) acc[j][i] = fmaf(hv, cvr[k][i], acc[j][i]);
+                        }
+                    }
+                }
+            }
+            for (int i = wave, pidx = 0; i < n_rec; i += kWaves, ++pidx) {
+                float v[CPL];
+                if (pidx < kRecentPre) {
+#pragma unroll
+                    for (int q = 0; q < kRecentPre; ++q)
+                        if (q == pidx)
+#pragma unroll
+                            for (int t = 0; t < CPL; ++t) v[t] = vpre[q][t];
+                } else {
+                    const RT* vr = rv + (int64_t)i * D + em * DSUB + ecomp;
+#pragma unroll
+                    for (int t = 0; t < CPL; ++t) v[t] = to_f32(vr[t]);
+                }
+#pragma unroll
+                for (int j = 0; j < QH; ++j) {
+                    const float p = rs[j * RS + i];
+#pragma unroll
+                    for (int t = 0; t < CPL; ++t) acc[j][t] = fmaf(p, v[t], acc[j][t]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < QH; ++j)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) ored[(wave * QH + j) * D + em * DSUB + ecomp + i] = acc[j][i];
+    }
+    __syncthreads();
+    // Partials are published with agent-scope stores, which write through the
+    // XCD-private L2, so the merging work-group on another XCD reads them from memory.
+    for (int e = tid; e < QH * D; e += kThreads) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s += ored[w * QH * D + e];
+        const int j = e / D;
+        publish(part + j * head_step + (e - j * D), s * a.fix_inv);
+    }
+    if (tid < QH) {
+        uint32_t lh = 0u;
+        float lr = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            lh += redu[w * QH + tid];
+            lr += red[w * QH + tid];
+        }
+        publish(part + tid * head_step + D, any ? mx[tid] : -INFINITY);
+        publish(part + tid * head_step + D + 1, ((float)lh + lr) * a.fix_inv);
+    }
+
+    // ---- 7. the last work-group of this unit merges every split's partial.
+    // Every wave waits for its stores to complete before the barrier; the counter
+    // increment that follows is therefore ordered after all of them.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (done == (uint32_t)(a.n_split - 1));
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    // Split maxima and sums to LDS (rs is free now), then every output element
+    // reads its n_split partial values with eight loads in flight.
+    const float* prow0 = a.partials + (int64_t)(b * a.Hq + hq0) * a.n_split * a.pstride;
+    float* pm = rs;                       // [QH][n_split]
+    float* pl = rs + QH * a.n_split;      // [QH][n_split]
+    for (int e = tid; e < QH * a.n_split; e += kThreads) {
+        const int j = e / a.n_split;
+        const int sp = e - j * a.n_split;
+        const float* ps = prow0 + j * head_step + (int64_t)sp * a.pstride;
+        pm[e] = collect(ps + D);
+        pl[e] = collect(ps + D + 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < QH * D; e += kThreads) {
+        const int j = e / D;
+        const int el = e - j * D;
+        const float* pmj = pm + j * a.n_split;
+        const float* plj = pl + j * a.n_split;
+        float mall = -INFINITY;
+        for (int sp = 0; sp < a.n_split; ++sp) mall = fmaxf(mall, pmj[sp]);
+        const int64_t orow = (int64_t)(b * a.Hq + hq0 + j);
+        if (mall == -INFINITY) {
+            a.out[orow * D + el] = 0.0f;
+            if (el == 0) a.lse[orow] = -INFINITY;
+            continue;
+        }
+        const float* pe = prow0 + j * head_step + el;
+        float l = 0.0f, o = 0.0f;
+        for (int s0 = 0; s0 < a.n_split; s0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sp = s0 + u < a.n_split ? s0 + u : a.n_split - 1;
+                v[u] = collect(pe + (int64_t)sp * a.pstride);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (s0 + u < a.n_split && pmj[s0 + u] != -INFINITY) {
+                    const float wgt = exp2f(pmj[s0 + u] - mall);
+                    l = fmaf(wgt, plj[s0 + u], l);
+                    o = fmaf(wgt, v[u], o);
+                }
+            }
+        }
+        a.out[orow * D + el] = o / l;
+        if (el == 0) a.lse[orow] = (mall + log2f(l)) * kLn2;
+    }
+    if (tid == 0) __hip_atomic_store(a.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int M, int DSUB, int QH, typename QT, typename RT>
+hipError_t launch_typed(const pqkv_dims& d, int32_t batch, const DecodePlan& plan, const DecodeArgs& in,
+                        hipStream_t stream) {
+    DecArgs k;
+    k.q = in.q;
+    k.cb_k = in.cb_k;
+    k.cb_v = in.cb_v;
+    k.codes_k = in.codes_k;
+    k.codes_v = in.codes_v;
+    k.t_cap = in.t_cap;
+    k.hist_len = in.hist_len;
+    k.max_hist = in.max_hist;
+    k.rk = in.rk;
+    k.rv = in.rv;
+    k.r_cap = in.r_cap;
+    k.recent_len = in.recent_len;
+    k.scale_log2 = in.scale_log2;
+    // Largest S with split_tokens * 2^S <= 2^31: a histogram cell and the weight sum
+    // stay below 2^31 even if every token had weight 1.
+    int S = 31;
+    for (int64_t t = plan.split_tokens; t > 1; t = (t + 1) / 2) --S;
+    k.fix_scale = ldexpf(1.0f, S);
+    k.fix_inv = ldexpf(1.0f, -S);
+    k.partials = in.partials;
+    k.counters = in.counters;
+    k.out = in.out;
+    k.lse = in.lse;
+    k.K = d.n_centroids;
+    k.Hq = d.n_q_heads;
+    k.Hkv = d.n_kv_heads;
+    k.n_groups = plan.n_groups;
+    k.n_split = plan.n_split;
+    k.rounds = plan.rounds;
+    k.pstride = plan.partial_stride;
+    k.split_tokens = plan.split_tokens;
+    const int64_t items = (int64_t)batch * d.n_kv_heads * plan.n_groups * plan.n_split;
+    const int64_t per_xcd = (items + 7) / 8;
+    k.n_items = (int)items;
+    k.per_xcd = (int)per_xcd;
+    hipLaunchKernelGGL((pq_decode_kernel<M, DSUB, QH, QT, RT>), dim3((unsigned)(per_xcd * 8)), dim3(kThreads), 0,
+                       stream, k);
+    return hipGetLastError();
+}
+
+template <int M, int DSUB, typename QT, typename RT>
+hipError_t launch_qh(const pqkv_dims& d, int32_t batch, const DecodePlan& plan, const DecodeArgs& a,
+                     hipStream_t stream) {
+    if constexpr (M <= 16) {
+        if (plan.qh == 4) return launch_typed<M, DSUB, 4, QT, RT>(d, batch, plan, a, stream);
+    }
+    if constexpr (M <= 32) {
+        if (plan.qh == 2) return launch_typed<M, DSUB, 2, QT, RT>(d, batch, plan, a, stream);
+    }
+    return launch_typed<M, DSUB, 1, QT, RT>(d, batch, plan, a, stream);
+}
+
+template <typename QT, typename RT>
+hipError_t launch_shape(const pqkv_dims& d, int32_t batch, const DecodePlan& plan, const DecodeArgs& a,
+                        hipStream_t stream) {
+    const int M = d.head_dim / d.d_sub;
+    if (M == 64) return launch_qh<64, 2, QT, RT>(d, batch, plan, a, stream);
+    if (M == 32 && d.d_sub == 4) return launch_qh<32, 4, QT, RT>(d, batch, plan, a, stream);
+    if (M == 32) return launch_qh<32, 2, QT, RT>(d, batch, plan, a, stream);
+    return launch_qh<16, 4, QT, RT>(d, batch, plan, a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const pqkv_dims& d, int32_t batch, pqkv_dtype qt, pqkv_dtype rt,
+                         const DecodePlan& plan, const DecodeArgs& a, hipStream_t stream) {
+    if (qt == PQKV_F16)
+        return rt == PQKV_F16 ? launch_shape<__half, __half>(d, batch, plan, a, stream)
+                              : launch_shape<__half, float>(d, batch, plan, a, stream);
+    return rt == PQKV_F16 ? launch_shape<float, __half>(d, batch, plan, a, stream)
+                          : launch_shape<float, float>(d, batch, plan, a, stream);
+}
+
+}  // namespace pqkv

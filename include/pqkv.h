@@ -1,0 +1,195 @@
+/*
+ * libpqkv -- product-quantised KV cache: encode and decode attention on MI355X (gfx950).
+ *
+ * The method is MILLION (DAC 2025), as described in its write-up ("MILLION:
+ * product-quantisation based KV-cache compression and decode acceleration"):
+ * every key/value head vector is split into subspaces of dimension 2 or 4
+ * (the paragraph after Fig. 5), each subspace is replaced by the uint8 index of
+ * its nearest codebook centroid when the prefill cache is written (Fig. 6
+ * paragraph), and decode attention scores the compressed history through an
+ * asymmetric-distance lookup table of query x codebook, computed apart from the
+ * attention over recent full-precision tokens and merged with it (Fig. 7
+ * paragraph), on a split-over-tokens flash-decoding base (Fig. 8 paragraph).
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates nothing and keeps no pointer after the enqueued work finishes.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the null stream); no
+ *     entry point synchronises the host.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     violation returns PQKV_ERR_INVALID / PQKV_ERR_UNSUPPORTED /
+ *     PQKV_ERR_WORKSPACE and enqueues nothing.  A failed launch returns
+ *     PQKV_ERR_HIP.  A device-side fault shows up at the caller's next
+ *     synchronisation.  No C++ exception crosses this interface.
+ *   - The library keeps no mutable global state; calls are thread-safe.
+ *
+ * Shapes and symbols
+ *   d = head_dim in {64, 128};  d_sub in {2, 4};  M = d / d_sub subspaces;
+ *   K = n_centroids in [2, 256];  Hq query heads, Hkv kv heads, Hq % Hkv == 0;
+ *   query head hq reads kv head hq / (Hq / Hkv).
+ *
+ * Codebook layout (fp32, one per (layer, kv head, tensor K or V)):
+ *   codebook[h][c][m][j]  = [Hkv][K][M][d_sub]   (centroid-major, subspace-minor)
+ *   Centroid c of subspace m of head h is the d_sub floats at ((h*K + c)*M + m)*d_sub.
+ *
+ * Code-cache layout (uint8, one byte per (token, subspace)):
+ *   codes[b][h] is a plane of t_cap*M bytes (t_cap a multiple of 64); planes are
+ *   dense: plane (b, h) starts at byte (b*Hkv + h) * t_cap * M.
+ *   Inside a plane, token t and subspace m sit at byte
+ *       tile  = t / 64,  l = t % 64,  p = (m - l) mod M,
+ *       off   = tile*64*M + (p / 16)*1024 + l*16 + (p % 16).
+ *   So a tile of 64 tokens is 64*M contiguous bytes; the 16-byte chunk i of the
+ *   64 tokens of a tile is one contiguous 1 KiB run (one token per 16 bytes),
+ *   and byte p of token slot l holds subspace (p + l) mod M.  Reading a tile
+ *   with one 16-byte load per lane is fully coalesced, and lanes that consume
+ *   byte p at the same time touch 64 different subspaces, which keeps the
+ *   on-chip table accesses free of bank conflicts.
+ */
+#ifndef PQKV_H
+#define PQKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PQKV_OK = 0,
+    PQKV_ERR_INVALID = 1,     /* a bad argument: null pointer, negative size, bad stride, bad enum */
+    PQKV_ERR_UNSUPPORTED = 2, /* a valid but unsupported shape (head_dim, d_sub, K, r_cap ...) */
+    PQKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than pqkv_decode_workspace_bytes */
+    PQKV_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} pqkv_status;
+
+typedef enum { PQKV_F16 = 0, PQKV_F32 = 1 } pqkv_dtype;
+
+typedef struct {
+    int32_t head_dim;    /* d: 64 or 128 */
+    int32_t d_sub;       /* subspace dimension: 2 or 4 */
+    int32_t n_centroids; /* K: 2..256 */
+    int32_t n_q_heads;   /* Hq >= 1 */
+    int32_t n_kv_heads;  /* Hkv >= 1, divides Hq */
+} pqkv_dims;
+
+/* Largest recent window (r_cap) pqkv_decode_attention accepts. */
+#define PQKV_MAX_RECENT 1024
+
+/*
+ * pqkv_encode -- nearest-centroid codes for a block of tokens (the online
+ * prefill quantisation of the Fig. 6 paragraph; the subspace split of the
+ * paragraph after Fig. 5).
+ *
+ * For every sequence b < n_seqs, token i < n_tokens, kv head h and subspace m:
+ *     code = argmin_c sum_j (x[b][i][h][m*d_sub + j] - codebook[h][c][m][j])^2,
+ * lowest c on exact ties, distances evaluated in fp32 as the sum of squared
+ * differences (no expanded |x|^2 - 2x.c + |c|^2 form).  The code is written to
+ * token position t_start + i of plane (b, h) of `codes`.
+ *
+ *   x            device, x_dtype (F16 or F32); element (b, i, h, e) at
+ *                x + b*x_seq_stride + i*x_tok_stride + h*x_head_stride + e (in elements);
+ *                strides >= 0, rows of d contiguous elements.
+ *   codebook     device fp32 [Hkv][K][M][d_sub] (layout above).
+ *   codes        device uint8, n_seqs consecutive sequences of Hkv planes of t_cap*M bytes.
+ *   t_cap        plane capacity in tokens, multiple of 64, t_start + n_tokens <= t_cap.
+ *   n_seqs, n_tokens may be 0 (nothing is enqueued).
+ * Only the bytes of the encoded tokens are written.  Errors: INVALID for null
+ * pointers with work to do, negative sizes, t_start + n_tokens > t_cap, t_cap
+ * not a multiple of 64, bad dtype; UNSUPPORTED for dims outside the ranges above.
+ */
+pqkv_status pqkv_encode(const pqkv_dims* dims, const void* x, pqkv_dtype x_dtype, int32_t n_seqs,
+                        int64_t n_tokens, int64_t x_seq_stride, int64_t x_tok_stride,
+                        int64_t x_head_stride, const float* codebook, uint8_t* codes, int64_t t_cap,
+                        int64_t t_start, hipStream_t stream);
+
+/*
+ * pqkv_build_lut -- the asymmetric-distance lookup table of the Fig. 7
+ * paragraph, materialised:
+ *     lut[b][hq][m][c] = sum_j q[b][hq][m*d_sub + j] * codebook_k[hq / g][c][m][j]
+ * in fp32, unscaled (no softmax scale).
+ *   q           device [batch][Hq][d] in q_dtype (F16 or F32), dense.
+ *   codebook_k  device fp32 [Hkv][K][M][d_sub].
+ *   lut         device fp32 [batch][Hq][M][K], dense, written whole.
+ * pqkv_decode_attention does not need this table: it builds the same table in
+ * on-chip memory.  Errors as for pqkv_encode.
+ */
+pqkv_status pqkv_build_lut(const pqkv_dims* dims, int32_t batch, const void* q, pqkv_dtype q_dtype,
+                           const float* codebook_k, float* lut, hipStream_t stream);
+
+/*
+ * Workspace bytes pqkv_decode_attention needs for these sizes.  Depends only on
+ * its arguments.  Returns 0 for invalid dims, batch <= 0 or max_hist_len < 0.
+ */
+size_t pqkv_decode_workspace_bytes(const pqkv_dims* dims, int32_t batch, int64_t max_hist_len);
+
+/*
+ * pqkv_decode_attention -- one decode step of attention for `batch` sequences
+ * over a PQ-compressed history plus a recent full-precision window (Fig. 7
+ * paragraph: history attention apart from new-token attention, ad-LUT scoring
+ * of the history; Fig. 8 paragraph: flash-decoding split over tokens).
+ *
+ * For query row (b, hq), h = hq / g, the result is ordinary softmax attention of
+ * q[b][hq] over the hist_len[b] history tokens of planes (b, h) -- key and value
+ * of token t being the centroids its K and V codes select -- followed by the
+ * recent_len[b] recent tokens of recent_k/v[b][h]:
+ *     s_i  = softmax_scale * q . key_i,
+ *     out  = sum_i exp(s_i - mu) value_i / sum_i exp(s_i - mu),   mu = max_i s_i,
+ *     lse  = mu + ln sum_i exp(s_i - mu).
+ * A row with no tokens gets out = 0 and lse = -inf.
+ *
+ *   q             device [batch][Hq][d], q_dtype, dense.
+ *   codebook_k/v  device fp32 [Hkv][K][M][d_sub].
+ *   codes_k/v     device uint8 cache planes (layout above), batch*Hkv planes of t_cap*M
+ *                 bytes, 16-byte aligned; only tokens < hist_len[b] are read.
+ *   hist_len      device int32 [batch], each in [0, max_hist_len].
+ *   max_hist_len  host bound on hist_len, <= t_cap; sizes the split-over-tokens grid.
+ *   recent_k/v    device [batch][Hkv][r_cap][d] in recent_dtype, dense; may be NULL if r_cap == 0.
+ *   recent_len    device int32 [batch], each in [0, r_cap]; may be NULL if r_cap == 0.
+ *   r_cap         0..PQKV_MAX_RECENT.
+ *   out           device fp32 [batch][Hq][d];  lse device fp32 [batch][Hq] (natural log).
+ *   workspace     device, >= pqkv_decode_workspace_bytes(dims, batch, max_hist_len) bytes,
+ *                 256-byte aligned.  It must be zero-filled before the first call that uses
+ *                 it (e.g. one hipMemset); every call leaves it ready for the next one.  It
+ *                 holds per-split partial results and per-(sequence, kv head) completion
+ *                 counters, so calls sharing one workspace must be ordered on one stream.
+ * Device-side lengths outside their bounds are clamped to them.  Errors: INVALID
+ * for null pointers, negative sizes, max_hist_len > t_cap, bad dtype;
+ * UNSUPPORTED for dims outside the ranges above or r_cap > PQKV_MAX_RECENT;
+ * WORKSPACE for a missing or short workspace.
+ */
+pqkv_status pqkv_decode_attention(const pqkv_dims* dims, int32_t batch, const void* q,
+                                  pqkv_dtype q_dtype, const float* codebook_k,
+                                  const float* codebook_v, const uint8_t* codes_k,
+                                  const uint8_t* codes_v, int64_t t_cap, const int32_t* hist_len,
+                                  int64_t max_hist_len, const void* recent_k, const void* recent_v,
+                                  pqkv_dtype recent_dtype, int64_t r_cap,
+                                  const int32_t* recent_len, float softmax_scale, float* out,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
+ * pqkv_merge -- log-sum-exp merge of two normalised attention states over
+ * disjoint token sets (the combination step of the Fig. 7 paragraph):
+ *     mu = max(lse_a, lse_b),  wa = exp(lse_a - mu),  wb = exp(lse_b - mu),
+ *     out = (wa*out_a + wb*out_b) / (wa + wb),  lse = mu + ln(wa + wb),
+ * row by row; a side with lse = -inf has weight 0; two such sides give out = 0,
+ * lse = -inf.
+ *   out_a/out_b/out  device fp32 [n_rows][head_dim];  lse_a/lse_b/lse device fp32 [n_rows].
+ *   out may alias out_a or out_b and lse may alias lse_a or lse_b (element-wise in place).
+ *   head_dim in 1..1024.
+ */
+pqkv_status pqkv_merge(int64_t n_rows, int32_t head_dim, const float* out_a, const float* lse_a,
+                       const float* out_b, const float* lse_b, float* out, float* lse,
+                       hipStream_t stream);
+
+/* Static description of a status code. */
+const char* pqkv_status_str(pqkv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQKV_H */

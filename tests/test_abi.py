@@ -1,0 +1,122 @@
+"""The C ABI without a GPU: the library loads, exports what include/pqkv.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def P():
+    import decode_attention_pq_amd as P
+
+    P.lib()
+    return P
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pqkv.h")).read()
+    return sorted(set(re.findall(r"\b(pqkv_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(P):
+    names = _declared()
+    assert {"pqkv_encode", "pqkv_build_lut", "pqkv_decode_attention", "pqkv_merge",
+            "pqkv_decode_workspace_bytes", "pqkv_status_str"} <= set(names)
+    for n in names:
+        assert hasattr(P.lib(), n), n
+
+
+def test_status_strings(P):
+    L = P.lib()
+    assert L.pqkv_status_str(0) == b"ok"
+    assert L.pqkv_status_str(3).startswith(b"workspace")
+    assert L.pqkv_status_str(99) == b"unknown status"
+
+
+def _d(P, *a):
+    return ctypes.byref(P.Dims(*a))
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+def test_encode_validation(P):
+    L = P.lib()
+    ok = (128, 2, 256, 32, 32)
+    args = lambda dims, n=10, t_cap=64, t_start=0, x=FAKE, dt=0: (
+        _d(P, *dims), x, dt, 1, n, 0, 4096, 128, FAKE, FAKE, t_cap, t_start, None)
+    assert L.pqkv_encode(*args((96, 2, 256, 32, 32))) == 2      # head_dim unsupported
+    assert L.pqkv_encode(*args((128, 3, 256, 32, 32))) == 1     # d_sub does not divide d... 128 % 3 != 0
+    assert L.pqkv_encode(*args((128, 8, 256, 32, 32))) == 2     # d_sub 8 unsupported
+    assert L.pqkv_encode(*args((128, 2, 257, 32, 32))) == 2     # K > 256
+    assert L.pqkv_encode(*args((128, 2, 256, 32, 5))) == 1      # Hq % Hkv
+    assert L.pqkv_encode(*args(ok, t_cap=100)) == 1             # t_cap not a multiple of 64
+    assert L.pqkv_encode(*args(ok, n=60, t_start=10)) == 1      # past capacity
+    assert L.pqkv_encode(*args(ok, x=None)) == 1                # null input
+    assert L.pqkv_encode(*args(ok, dt=7)) == 1                  # bad dtype
+    assert L.pqkv_encode(*args(ok, n=0, x=None)) == 0           # nothing to do
+    assert L.pqkv_encode(*args(ok, x=ctypes.c_void_p(0x10002))) == 1  # misaligned rows
+    assert L.pqkv_encode(None, FAKE, 0, 1, 10, 0, 4096, 128, FAKE, FAKE, 64, 0, None) == 1
+
+
+def test_decode_validation(P):
+    L = P.lib()
+    dims = (128, 2, 256, 32, 32)
+    ws_need = L.pqkv_decode_workspace_bytes(_d(P, *dims), 1, 32768)
+    assert ws_need > 0
+
+    def call(dims=dims, batch=1, t_cap=32768, maxh=32768, r_cap=128, ws=FAKE, wsb=None, codes=FAKE, qdt=0,
+             scale=0.088):
+        return L.pqkv_decode_attention(
+            _d(P, *dims), batch, FAKE, qdt, FAKE, FAKE, codes, codes, t_cap, FAKE, maxh, FAKE, FAKE, 0, r_cap,
+            FAKE, scale, FAKE, FAKE, ws, ws_need if wsb is None else wsb, None)
+
+    assert call(ws=None) == 3
+    assert call(wsb=ws_need - 1) == 3
+    assert call(ws=ctypes.c_void_p(0x10010)) == 3        # workspace not 256-byte aligned
+    assert call(maxh=40000) == 1                          # longer than the capacity
+    assert call(t_cap=1000, maxh=900) == 1                # capacity not a multiple of 64
+    assert call(r_cap=2000) == 2                          # recent window too large
+    assert call(codes=ctypes.c_void_p(0x10004)) == 1      # misaligned code planes
+    assert call(qdt=5) == 1
+    assert call(batch=-1) == 1
+    assert call(batch=0) == 0
+    assert call(scale=float("nan")) == 1
+    assert call(dims=(128, 2, 1, 32, 32)) == 2            # K < 2
+    assert call(dims=(128, 2, 256, 0, 32)) == 1
+
+
+def test_workspace_formula(P):
+    L = P.lib()
+    # partials (132 floats per query head and split) padded to 256 bytes, then one
+    # u32 completion counter per (sequence, kv head, query-head group), padded
+    # config-2 shape: 32 kv heads, one query head each, 8 splits of 4096 tokens
+    assert L.pqkv_decode_workspace_bytes(_d(P, 128, 2, 256, 32, 32), 1, 32768) == 32 * 8 * 132 * 4 + 256
+    # no history: one split per unit for the recent window
+    assert L.pqkv_decode_workspace_bytes(_d(P, 128, 2, 256, 32, 32), 1, 0) == 32 * 1 * 132 * 4 + 256
+    assert L.pqkv_decode_workspace_bytes(_d(P, 96, 2, 256, 32, 32), 1, 100) == 0
+    assert L.pqkv_decode_workspace_bytes(_d(P, 128, 2, 256, 32, 32), 0, 100) == 0
+    # GQA 32/8 at d_sub=4: two query heads per work-group, 32 splits of 4096 tokens
+    assert L.pqkv_decode_workspace_bytes(_d(P, 128, 4, 256, 32, 8), 1, 131072) == 32 * 32 * 132 * 4 + 256
+
+
+def test_merge_validation(P):
+    L = P.lib()
+    assert L.pqkv_merge(-1, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.pqkv_merge(4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.pqkv_merge(4, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert L.pqkv_merge(0, 128, None, None, None, None, None, None, None) == 0
+    assert L.pqkv_merge(4, 128, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "decode_attention_pq_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", src), f"{f} mentions the oracle"

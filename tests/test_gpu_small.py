@@ -1,0 +1,217 @@
+"""GPU parity on small shapes: every entry point of libpqkv against the CPU oracle.
+
+Sizes are small enough for the oracle to finish in seconds but span several
+64-token tiles, several history splits and ragged tails, and cover the edge
+cases: empty history, empty recent window, both empty, one token, GQA groups,
+both subspace dimensions and head sizes, fp16 and fp32 inputs, duplicate
+centroids and unaligned append positions.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import synthkv
+from pqkv_testlib import (check_attention, check_codes, dims_for, run_gpu_decode, run_gpu_encode,
+                          softmax_scale, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _outlier_values(seed, shape, dtype):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape).astype(np.float32)
+    x[..., :3] *= 10.0
+    x[rng.random(shape) < 0.01] *= 20.0
+    return x.astype(dtype)
+
+
+def _codebook(seed, H, K, M, dsub, scale=3.0):
+    return (np.random.default_rng(seed).standard_normal((H, K, M, dsub)) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("d,dsub", [(128, 2), (128, 4), (64, 2), (64, 4)])
+@pytest.mark.parametrize("K", [256, 37])
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_encode_matches_oracle(d, dsub, K, dtype):
+    H, N, n_seqs, t_cap, t_start = 3, 300, 2, 384, 17
+    M = d // dsub
+    x = _outlier_values(d * 7 + K, (n_seqs, N, H, d), dtype)
+    cb = _codebook(K + dsub, H, K, M, dsub)
+    dims = dims_for(d, dsub, K, H, H)
+    fill = np.full((n_seqs, H, t_cap * M), 0xAB, np.uint8)
+    planes = run_gpu_encode(dims, x, cb, n_seqs, t_cap, t_start, init_codes=fill)
+    off = oracle.code_offsets(M, t_cap)
+    written = np.zeros(t_cap * M, bool)
+    written[off[t_start:t_start + N].ravel()] = True
+    assert np.all(planes[..., ~written] == 0xAB), "bytes outside the encoded tokens changed"
+    for s in range(n_seqs):
+        ref, d1, d2, amb = oracle.encode(x[s], cb)
+        got = oracle.untile_codes(planes[s], t_start + N, M)[:, t_start:].transpose(1, 0, 2)
+        check_codes(got, x[s], cb, ref, d1, d2)
+
+
+def test_encode_duplicate_centroids_lowest_index():
+    d, dsub, K, H = 128, 2, 64, 2
+    M = d // dsub
+    cb = _codebook(5, H, K, M, dsub)
+    cb[:, 40] = cb[:, 7]  # duplicates: index 7 must win
+    cb[:, 63] = cb[:, 7]
+    x = np.repeat(cb[:, 7][None], 70, axis=0).reshape(70, H, d).astype(np.float32)
+    planes = run_gpu_encode(dims_for(d, dsub, K, H, H), x[None], cb, 1, 128)
+    got = oracle.untile_codes(planes[0], 70, M)
+    assert np.all(got == 7)
+
+
+def test_encode_deterministic():
+    d, dsub, K, H = 128, 2, 256, 4
+    x = _outlier_values(3, (1, 1000, H, d), np.float16)
+    cb = _codebook(4, H, K, d // dsub, dsub)
+    dims = dims_for(d, dsub, K, H, H)
+    a = run_gpu_encode(dims, x, cb, 1, 1024)
+    b = run_gpu_encode(dims, x, cb, 1, 1024)
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("d,dsub,Hq,Hkv", [(128, 2, 4, 2), (128, 4, 8, 2), (64, 2, 3, 3), (64, 4, 8, 2)])
+@pytest.mark.parametrize("qdtype", [np.float16, np.float32])
+def test_build_lut_matches_oracle(d, dsub, Hq, Hkv, qdtype):
+    import torch
+
+    import decode_attention_pq_amd as P
+
+    K, B = 200, 3
+    M = d // dsub
+    q = synthkv.small_normal(11, (B, Hq, d), qdtype)
+    cb = _codebook(12, Hkv, K, M, dsub)
+    dims = dims_for(d, dsub, K, Hq, Hkv)
+    lut = torch.full((B, Hq, M, K), np.nan, dtype=torch.float32, device="cuda")
+    P.build_lut(dims, to_dev(q), to_dev(cb), lut)
+    torch.cuda.synchronize()
+    got = lut.cpu().numpy()
+    ref = oracle.lut(q, cb, Hq // Hkv)
+    g = Hq // Hkv
+    qs = np.abs(q.astype(np.float64)).reshape(B, Hq, M, dsub)
+    bound = np.einsum("bhmj,hcmj->bhmc", qs, np.abs(cb[np.arange(Hq) // g]).astype(np.float64))
+    assert np.all(np.abs(got - ref) <= 1e-6 * bound + 1e-30)
+
+
+DECODE_CASES = [
+    # d, dsub, K, Hq, Hkv, hist_len, recent_len, r_cap, dtype
+    (128, 2, 256, 4, 4, (700,), (5,), 8, np.float16),            # one split, ragged tail
+    (128, 2, 256, 2, 1, (5000, 0), (3, 0), 4, np.float16),        # many splits; second row empty
+    (128, 2, 256, 2, 2, (0, 1, 64, 65), (7, 0, 1, 0), 8, np.float16),  # empty history / one token / tile edges
+    (128, 2, 37, 8, 2, (3000, 1025), (0, 12), 16, np.float16),    # GQA g=4 with M=64 (two groups), K=37
+    (128, 4, 256, 8, 2, (4097, 2048), (16, 1), 16, np.float16),   # d_sub=4: two query heads per work-group
+    (64, 2, 16, 4, 4, (512,), (16,), 16, np.float32),             # the tiny shape, fp32
+    (64, 4, 64, 8, 2, (1500, 3), (2, 2), 4, np.float32),          # M=16: four query heads per work-group
+    (128, 2, 256, 2, 2, (2000, 40), (0, 0), 0, np.float16),       # no recent window at all
+    (128, 2, 256, 1, 1, (0,), (0,), 4, np.float16),               # nothing cached
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[f"case{i}" for i in range(len(DECODE_CASES))])
+def test_decode_matches_oracle(case):
+    d, dsub, K, Hq, Hkv, hist, rec, r_cap, dt = case
+    B = len(hist)
+    M = d // dsub
+    t_cap = max(64, -(-max(hist) // 64) * 64)
+    seed = sum(hist) + 31 * K + d
+    q = synthkv.small_normal(seed, (B, Hq, d), dt)
+    cbk = _codebook(seed + 1, Hkv, K, M, dsub, 1.0)
+    cbv = _codebook(seed + 2, Hkv, K, M, dsub, 1.0)
+    ck = synthkv.small_codes(seed + 3, (B, Hkv, t_cap, M), K)
+    cv = synthkv.small_codes(seed + 4, (B, Hkv, t_cap, M), K)
+    rk = synthkv.small_normal(seed + 5, (B, Hkv, r_cap, d), dt)
+    rv = synthkv.small_normal(seed + 6, (B, Hkv, r_cap, d), dt)
+    scale = softmax_scale(d)
+    ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, hist, rk, rv, rec, scale)
+    pk, pv = oracle.tile_codes(ck, t_cap), oracle.tile_codes(cv, t_cap)
+    dims = dims_for(d, dsub, K, Hq, Hkv)
+    out, lse = run_gpu_decode(dims, q, cbk, cbv, pk, pv, t_cap, hist, rk if r_cap else None,
+                              rv if r_cap else None, rec, scale)
+    check_attention(out, lse, ref_out, ref_lse)
+    if max(hist) > 0:  # a looser host bound on the history length gives the same result
+        out2, lse2 = run_gpu_decode(dims, q, cbk, cbv, pk, pv, t_cap, hist, rk if r_cap else None,
+                                    rv if r_cap else None, rec, scale, max_hist=t_cap)
+        check_attention(out2, lse2, ref_out, ref_lse)
+
+
+def test_tiny_workload_end_to_end():
+    """The Tiny workload: codebooks fit by 10 Lloyd iterations on its own history,
+    GPU encode bit-exact with the oracle, GPU decode within tolerance."""
+    w = synthkv.WORKLOADS["tiny"]
+    M, d = w.n_sub, w.head_dim
+    dims = dims_for(d, w.d_sub, w.n_centroids, w.n_q_heads, w.n_kv_heads)
+    t_cap = w.t_cap
+    cbs, codes = {}, {}
+    for tensor in ("k", "v"):
+        cb = oracle.fit_workload_codebooks(w, 0, tensor, synthkv)
+        x = synthkv.history_kv(w, 0, tensor, 0)
+        ref, d1, d2, _ = oracle.encode(x, cb)
+        planes = run_gpu_encode(dims, x[None], cb, 1, t_cap)
+        got = oracle.untile_codes(planes[0], w.hist_len[0], M).transpose(1, 0, 2)
+        check_codes(got, x, cb, ref, d1, d2)
+        cbs[tensor] = cb
+        codes[tensor] = ref.transpose(1, 0, 2)[None]  # [1, H, T, M]
+    q = synthkv.queries(w)
+    rk, rv = synthkv.recent_kv(w, 0, "k"), synthkv.recent_kv(w, 0, "v")
+    scale = softmax_scale(d)
+    ref_out, ref_lse = oracle.decode_exact(q, cbs["k"], cbs["v"], codes["k"], codes["v"], w.hist_len, rk, rv,
+                                           [w.recent_len], scale)
+    out, lse = run_gpu_decode(dims, q, cbs["k"], cbs["v"], oracle.tile_codes(codes["k"], t_cap),
+                              oracle.tile_codes(codes["v"], t_cap), t_cap, w.hist_len, rk, rv, [w.recent_len],
+                              scale)
+    check_attention(out, lse, ref_out, ref_lse)
+
+
+def test_merge_matches_oracle():
+    import torch
+
+    import decode_attention_pq_amd as P
+
+    rng = np.random.default_rng(21)
+    n, d = 37, 128
+    oa, ob = rng.standard_normal((n, d)).astype(np.float32), rng.standard_normal((n, d)).astype(np.float32)
+    la, lb = (rng.standard_normal(n) * 5).astype(np.float32), (rng.standard_normal(n) * 5).astype(np.float32)
+    la[3] = -np.inf
+    lb[4] = -np.inf
+    la[5] = lb[5] = -np.inf
+    ref_o, ref_l = oracle.merge_states(oa, la, ob, lb)
+    A, LA, Bt, LB = to_dev(oa), to_dev(la), to_dev(ob), to_dev(lb)
+    out = torch.empty_like(A)
+    lse = torch.empty_like(LA)
+    P.merge(A, LA, Bt, LB, out, lse)
+    torch.cuda.synchronize()
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, rtol=1e-5, lse_rtol=1e-6)
+    P.merge(A, LA, Bt, LB, A, LA)  # in place over the first state
+    torch.cuda.synchronize()
+    check_attention(A.cpu().numpy(), LA.cpu().numpy(), ref_o, ref_l, rtol=1e-5, lse_rtol=1e-6)
+
+
+def test_two_step_decode_merges_like_one():
+    """Splitting the recent window off into a second state and merging with
+    pqkv_merge reproduces the single call (blockwise history/new-token attention)."""
+    import torch
+
+    import decode_attention_pq_amd as P
+
+    d, dsub, K, H = 128, 2, 256, 4
+    M = d // dsub
+    T, R, t_cap = 900, 12, 960
+    q = synthkv.small_normal(1, (1, H, d), np.float16)
+    cbk, cbv = _codebook(2, H, K, M, dsub, 1.0), _codebook(3, H, K, M, dsub, 1.0)
+    ck, cv = synthkv.small_codes(4, (1, H, t_cap, M), K), synthkv.small_codes(5, (1, H, t_cap, M), K)
+    rk, rv = synthkv.small_normal(6, (1, H, R, d), np.float16), synthkv.small_normal(7, (1, H, R, d), np.float16)
+    scale = softmax_scale(d)
+    dims = dims_for(d, dsub, K, H, H)
+    pk, pv = oracle.tile_codes(ck, t_cap), oracle.tile_codes(cv, t_cap)
+    o1, l1 = run_gpu_decode(dims, q, cbk, cbv, pk, pv, t_cap, [T], None, None, [0], scale)
+    empty = np.zeros((1, H, t_cap * M), np.uint8)
+    o2, l2 = run_gpu_decode(dims, q, cbk, cbv, empty, empty, t_cap, [0], rk, rv, [R], scale)
+    out, lse = torch.empty(H, d, device="cuda"), torch.empty(H, device="cuda")
+    P.merge(to_dev(o1[0]), to_dev(l1[0]), to_dev(o2[0]), to_dev(l2[0]), out, lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, [T], rk, rv, [R], scale)
+    check_attention(out.cpu().numpy()[None], lse.cpu().numpy()[None], ref_out, ref_lse)
