@@ -50,20 +50,23 @@ static double sqdist(const double *x, const double *c, int dsub) {
 
 /* Nearest centroid with lowest-index tie-break; also the runner-up distance
  * (the smallest distance over every other index, so a duplicate centroid makes
- * it equal to the best). */
+ * it equal to the best).  One pass: a strictly smaller distance takes the best
+ * slot and pushes the old best to runner-up; anything else can only lower the
+ * runner-up. */
 static void nearest(const double *x, const double *C, int K, int dsub,
                     int32_t *code, double *d1, double *d2) {
     int best = 0;
     double bd = sqdist(x, C, dsub);
-    for (int c = 1; c < K; ++c) {
-        double dc = sqdist(x, C + (int64_t)c * dsub, dsub);
-        if (dc < bd) { bd = dc; best = c; }
-    }
     double second = INFINITY;
-    for (int c = 0; c < K; ++c) {
-        if (c == best) continue;
-        double dc = sqdist(x, C + (int64_t)c * dsub, dsub);
-        if (dc < second) second = dc;
+    for (int c = 1; c < K; ++c) {
+        const double dc = sqdist(x, C + (int64_t)c * dsub, dsub);
+        if (dc < bd) {
+            second = bd;
+            bd = dc;
+            best = c;
+        } else if (dc < second) {
+            second = dc;
+        }
     }
     *code = best;
     *d1 = bd;

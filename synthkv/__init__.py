@@ -18,8 +18,10 @@ then rounded to fp16.  The clustered outliers of the same figure are not
 modelled.
 
 Random streams: every array comes from its own
-``np.random.default_rng(SeedSequence([seed, layer, tensor, purpose, b]))``
-so that arrays are independent of generation order.
+``SeedSequence([seed, layer, tensor, purpose, b])``: normals from torch's CPU
+generator seeded by it (same values for any thread count), everything else
+from ``np.random.default_rng`` on it, so arrays are independent of generation
+order.
 """
 from __future__ import annotations
 
@@ -140,23 +142,55 @@ def outlier_channels(w: Workload, layer: int, tensor: str) -> np.ndarray:
     return np.stack([g.choice(w.head_dim, N_OUTLIER_CHANNELS, replace=False) for _ in range(w.n_kv_heads)])
 
 
+def _to_dtype(x: np.ndarray, dtype) -> np.ndarray:
+    """Round float32 to the workload dtype (IEEE round-to-nearest-even)."""
+    if dtype == np.float32:
+        return x
+    import torch
+
+    return torch.from_numpy(x).to(torch.float16).numpy()
+
+
+def _normal(seed_seq: np.random.SeedSequence, shape) -> np.ndarray:
+    """N(0,1) float32 from torch's seeded CPU generator (fast, and the same
+    values whatever the number of threads)."""
+    import torch
+
+    g = torch.Generator().manual_seed(int(seed_seq.generate_state(1, np.uint64)[0] >> np.uint64(1)))
+    return torch.randn(shape, generator=g, dtype=torch.float32).numpy()
+
+
+def bernoulli_positions(g: np.random.Generator, n: int, p: float) -> np.ndarray:
+    """Indices of successes of n i.i.d. Bernoulli(p) trials, drawn as geometric gaps."""
+    out, pos = [], -1
+    while True:
+        k = max(1024, int((n - pos) * p * 1.1) + 64)
+        c = pos + np.cumsum(g.geometric(p, size=k))
+        out.append(c[c < n])
+        if c[-1] >= n:
+            break
+        pos = int(c[-1])
+    return np.concatenate(out)
+
+
 def kv_values(w: Workload, layer: int, tensor: str, purpose: str, n_tokens: int, b: int = 0) -> np.ndarray:
     """Token-major K or V values [n_tokens, n_kv_heads, head_dim] in the workload dtype."""
-    g = stream(w.seed, layer, tensor, purpose, b)
-    x = g.standard_normal((n_tokens, w.n_kv_heads, w.head_dim), dtype=np.float32)
+    ss = np.random.SeedSequence([w.seed, layer, TENSOR[tensor], PURPOSE[purpose], b])
+    x = _normal(ss, (n_tokens, w.n_kv_heads, w.head_dim))
     if w.outliers:
         ch = outlier_channels(w, layer, tensor)
         for h in range(w.n_kv_heads):
             x[:, h, ch[h]] *= CHANNEL_SCALE
-        mask = g.random((n_tokens, w.n_kv_heads, w.head_dim), dtype=np.float32) < POINT_PROB
-        x[mask] *= POINT_SCALE
-    return x.astype(w.np_dtype)
+        g = np.random.default_rng(ss.spawn(1)[0])
+        flat = x.reshape(-1)
+        flat[bernoulli_positions(g, flat.size, POINT_PROB)] *= POINT_SCALE
+    return _to_dtype(x, w.np_dtype)
 
 
 def queries(w: Workload, layer: int = 0) -> np.ndarray:
     """Decode queries [batch, n_q_heads, head_dim], N(0,1), no outliers."""
-    g = stream(w.seed, layer, "q", "query")
-    return g.standard_normal((w.batch, w.n_q_heads, w.head_dim), dtype=np.float32).astype(w.np_dtype)
+    ss = np.random.SeedSequence([w.seed, layer, TENSOR["q"], PURPOSE["query"], 0])
+    return _to_dtype(_normal(ss, (w.batch, w.n_q_heads, w.head_dim)), w.np_dtype)
 
 
 def recent_kv(w: Workload, layer: int, tensor: str) -> np.ndarray:
@@ -209,7 +243,7 @@ def small_normal(seed: int, shape, dtype=np.float32) -> np.ndarray:
 
 def small_codes(seed: int, shape, n_centroids: int) -> np.ndarray:
     """Uniform random codes in [0, n_centroids) as uint8."""
-    return np.random.default_rng(seed).integers(0, n_centroids, size=shape, dtype=np.int64).astype(np.uint8)
+    return np.random.default_rng(seed).integers(0, n_centroids, size=shape, dtype=np.uint8)
 
 
 def grid_values(seed: int, shape, levels=(-1.5, -0.5, 0.5, 1.5), dtype=np.float32) -> np.ndarray:

@@ -100,8 +100,8 @@ def test_workspace_formula(P):
     assert L.pqkv_decode_workspace_bytes(_d(P, 128, 2, 256, 32, 32), 1, 0) == 32 * 1 * 132 * 4 + 256
     assert L.pqkv_decode_workspace_bytes(_d(P, 96, 2, 256, 32, 32), 1, 100) == 0
     assert L.pqkv_decode_workspace_bytes(_d(P, 128, 2, 256, 32, 32), 0, 100) == 0
-    # GQA 32/8 at d_sub=4: two query heads per work-group, 32 splits of 4096 tokens
-    assert L.pqkv_decode_workspace_bytes(_d(P, 128, 4, 256, 32, 8), 1, 131072) == 32 * 32 * 132 * 4 + 256
+    # GQA 32/8 at d_sub=4: two query heads per work-group, 16 splits of 8192 tokens
+    assert L.pqkv_decode_workspace_bytes(_d(P, 128, 4, 256, 32, 8), 1, 131072) == 32 * 16 * 132 * 4 + 256
 
 
 def test_merge_validation(P):
