@@ -110,13 +110,36 @@ __device__ inline float collect(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Code tiles are read once per call: non-temporal loads keep them from evicting
+// the codebooks and the kernel's own code from the caches.
 template <int NCH>
-__device__ inline void load_tile(uint4 (&cw)[NCH], const uint8_t* __restrict__ plane, int64_t tile, int lane,
+__device__ inline void load_tile(u32x4 (&cw)[NCH], const uint8_t* __restrict__ plane, int64_t tile, int lane,
                                  bool ok) {
     const uint8_t* p = ok ? plane + tile * (kTileTokens * NCH * 16) : reinterpret_cast<const uint8_t*>(g_zero_block);
     p += lane * 16;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) cw[c] = *reinterpret_cast<const uint4*>(p + c * (kTileTokens * 16));
+    for (int c = 0; c < NCH; ++c)
+        cw[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + c * (kTileTokens * 16)));
+}
+
+__device__ inline void load4(const float* p, float (&v)[4]) {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    v[0] = t.x;
+    v[1] = t.y;
+    v[2] = t.z;
+    v[3] = t.w;
+}
+
+__device__ inline void load4(const __half* p, float (&v)[4]) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    const float2 a = __half22float2(*reinterpret_cast<const __half2*>(&t.x));
+    const float2 b = __half22float2(*reinterpret_cast<const __half2*>(&t.y));
+    v[0] = a.x;
+    v[1] = a.y;
+    v[2] = b.x;
+    v[3] = b.y;
 }
 
 struct DecArgs {
@@ -139,7 +162,7 @@ struct DecArgs {
     uint32_t* counters;
     float* out;
     float* lse;
-    int K, Hq, Hkv, n_groups, n_split, rounds, pstride, n_items, per_xcd;
+    int K, Hq, Hkv, n_groups, n_split, rounds, pstride, n_items;
     int64_t split_tokens;
 };
 
@@ -155,12 +178,10 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     constexpr int CPL = D / 64;                // epilogue: output components per lane
     constexpr int CPER = kLdsRows / kWaves;    // epilogue: centroids per wave
     static_assert(QH * M <= kRow, "query-head group must fit one LDS row");
-    static_assert(2 * kMaxSplits <= RS, "the merge keeps split maxima and sums in rs");
 
     // LDS: histogram (u32) at byte 0, LUT at byte 65536, then the small buffers.
     __shared__ float lds[2 * kLdsRows * kRow];
     __shared__ float ored[kWaves * QH * D];     // per-wave output partials
-    __shared__ float qs[QH * D];                // query * scale * log2(e)
     __shared__ float rs[QH * RS];               // recent scores, then weights * 2^S
     __shared__ float red[kWaves * QH];
     __shared__ uint32_t redu[kWaves * QH];
@@ -172,10 +193,12 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    // XCD-aware work mapping: ids that share an XCD (id mod 8) get contiguous items
+    // XCD-aware work mapping: work-group ids that share an XCD (id mod 8) take
+    // contiguous items, so all splits of one kv head meet in one L2.  The grid has
+    // exactly n_items work-groups; XCD x holds ceil((n_items - x) / 8) of them.
     const int L = blockIdx.x;
-    const int item = (L & 7) * a.per_xcd + (L >> 3);
-    if (item >= a.n_items) return;
+    const int xcd = L & 7;
+    const int item = xcd * (a.n_items >> 3) + (xcd < (a.n_items & 7) ? xcd : (a.n_items & 7)) + (L >> 3);
     const int unit = item / a.n_split;
     const int split = item - unit * a.n_split;
     const int grp = unit % a.n_groups;
@@ -185,18 +208,62 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     const int hq0 = h * (a.Hq / a.Hkv) + grp * QH;
     const int K = a.K;
 
-    int64_t T = a.hist_len[b];
-    T = T < 0 ? 0 : (T > a.max_hist ? a.max_hist : T);
+    // The lengths come through the vector memory path: scalar loads return out of
+    // order, so waiting for one would also wait for every later scalar load.  They
+    // are used only after the length-independent loads below have been issued.
+    const int T_in = __hip_atomic_load(const_cast<int32_t*>(a.hist_len + b), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    const int R_in = a.recent_len ? __hip_atomic_load(const_cast<int32_t*>(a.recent_len + b), __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0;
     const int64_t t0 = (int64_t)split * a.split_tokens;
+    const int64_t tile0 = t0 / kTileTokens;
+    const int rounds = a.rounds;
+
+    // ---- 1. loads in the order they are needed (a wave's loads retire in issue
+    //         order): this thread's query values, the codebook values of this
+    //         thread's LUT entries, the first recent rows, the first tiles.
+    //         LUT entries: thread t builds subspaces [mg*EPL, mg*EPL + EPL) of
+    //         centroids c = (t + k*512) / (M/EPL), from one 16-byte load each.
+    constexpr int EPL = 4 / DSUB;
+    constexpr int LUT_LOADS = kLdsRows * M / EPL / kThreads;
+    const int mg = tid % (M / EPL);
+    const QT* qrow = static_cast<const QT*>(a.q) + (int64_t)(b * a.Hq + hq0) * D;
+    float ql[QH][4];       // q elements [4*mg, 4*mg + 4) of each head, for the LUT
+    float qr[QH][D / 64];  // q elements lane + 64k of each head, for the recent scores
+#pragma unroll
+    for (int j = 0; j < QH; ++j) {
+        load4(qrow + j * D + 4 * mg, ql[j]);
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) qr[j][k] = to_f32(qrow[j * D + lane + 64 * k]);
+    }
+    float4 cbq[LUT_LOADS];
+    {
+        const float* cbh = a.cb_k ? a.cb_k + (int64_t)h * K * M * DSUB + mg * 4
+                                  : reinterpret_cast<const float*>(g_zero_block);
+        const int cstride = a.cb_k ? M * DSUB : 0;
+#pragma unroll
+        for (int k = 0; k < LUT_LOADS; ++k) {
+            int c = (tid + k * kThreads) / (M / EPL);
+            c = c < K ? c : K - 1;
+            cbq[k] = *reinterpret_cast<const float4*>(cbh + (int64_t)c * cstride);
+        }
+    }
+    // Keep the scheduler from hoisting later loads above the codebook loads (the LUT
+    // would then wait for them too); the loads below also depend on the sequence
+    // lengths, whose fetch the codebook loads overlap.
+    __builtin_amdgcn_sched_barrier(0);
+    int T_v = T_in, R_v = R_in;
+    asm volatile("" : "+v"(T_v), "+v"(R_v));  // first use of the lengths: here, not earlier
+    int64_t T = T_v;
+    T = T < 0 ? 0 : (T > a.max_hist ? a.max_hist : T);
     const int64_t t1 = T < t0 + a.split_tokens ? T : t0 + a.split_tokens;
-    int R = a.recent_len ? a.recent_len[b] : 0;
+    int R = R_v;
     R = R < 0 ? 0 : (R > a.r_cap ? (int)a.r_cap : R);
     const int rs_per = (R + a.n_split - 1) / a.n_split;
     const int r0 = split * rs_per;
     const int n_rec = R - r0 < rs_per ? (R - r0 > 0 ? R - r0 : 0) : rs_per;
     const bool has_hist = t0 < t1;
-    const int64_t tile0 = t0 / kTileTokens;
-    const int rounds = a.rounds;
 
     const int64_t plane_off = ((int64_t)b * a.Hkv + h) * a.t_cap * M;
     const uint8_t* plane_k = a.codes_k + plane_off;
@@ -209,14 +276,9 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         const int r = s < RW ? s : s - RW;
         return r < rounds && step_tile(s) * kTileTokens < t1;
     };
-    auto issue = [&](uint4 (&slot)[NCH], int s) {
+    auto issue = [&](u32x4 (&slot)[NCH], int s) {
         load_tile<NCH>(slot, s < RW ? plane_k : plane_v, step_tile(s), lane, step_ok(s));
     };
-
-    // ---- 1. loads in the order they are needed (a wave's loads retire in issue
-    //         order): query, the first recent rows, codebook values, first tiles
-    const QT* qrow = static_cast<const QT*>(a.q) + (int64_t)(b * a.Hq + hq0) * D;
-    const float qval = to_f32(qrow[tid < QH * D ? tid : 0]) * a.scale_log2;
     const RT* rk = static_cast<const RT*>(a.rk) + (((int64_t)b * a.Hkv + h) * a.r_cap + r0) * D;
     const RT* rv = static_cast<const RT*>(a.rv) + (((int64_t)b * a.Hkv + h) * a.r_cap + r0) * D;
     const RT* rzero = reinterpret_cast<const RT*>(g_zero_block);
@@ -228,40 +290,33 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 #pragma unroll
         for (int k = 0; k < D / 64; ++k) kpre[p][k] = to_f32(row[i < n_rec ? 64 * k : 0]);
     }
-    float cbv_reg[LUT_PER_THREAD][DSUB];
-    const float* cbh = a.cb_k ? a.cb_k + (int64_t)h * K * M * DSUB : reinterpret_cast<const float*>(g_zero_block);
-    const int cstride = a.cb_k ? M * DSUB : 0;
-#pragma unroll
-    for (int k = 0; k < LUT_PER_THREAD; ++k) {
-        const int e = tid + k * kThreads;
-        int c = e / M;
-        const int m = a.cb_k ? e - c * M : 0;
-        c = c < K ? c : K - 1;
-        const float* cc = cbh + (int64_t)c * cstride + m * DSUB;
-#pragma unroll
-        for (int i = 0; i < DSUB; ++i) cbv_reg[k][i] = cc[i];
-    }
-    uint4 ring[NSLOT][NCH];
+    u32x4 ring[NSLOT][NCH];
 #pragma unroll
     for (int s = 0; s < P; ++s) issue(ring[s], s);
-    if (tid < QH * D) qs[tid] = qval;
-    __syncthreads();
 
     // ---- 2. ad-LUT in LDS, recent-window scores, per-lane subspace offsets
+#pragma unroll
+    for (int j = 0; j < QH; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ql[j][i] *= a.scale_log2;
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) qr[j][k] *= a.scale_log2;
+    }
     if (has_hist) {
 #pragma unroll
-        for (int k = 0; k < LUT_PER_THREAD; ++k) {
-            const int e = tid + k * kThreads;
-            const int c = e / M;
-            const int m = e - c * M;
+        for (int k = 0; k < LUT_LOADS; ++k) {
+            const int c = (tid + k * kThreads) / (M / EPL);
             if (c < K) {
+                const float cv[4] = {cbq[k].x, cbq[k].y, cbq[k].z, cbq[k].w};
 #pragma unroll
                 for (int j = 0; j < QH; ++j) {
-                    const float* qq = qs + j * D + m * DSUB;
-                    float s = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < DSUB; ++i) s = fmaf(qq[i], cbv_reg[k][i], s);
-                    table[c * kRow + j * M + m] = s;
+                    for (int t = 0; t < EPL; ++t) {
+                        float s = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < DSUB; ++i) s = fmaf(ql[j][t * DSUB + i], cv[t * DSUB + i], s);
+                        table[c * kRow + j * M + mg * EPL + t] = s;
+                    }
                 }
             }
         }
@@ -282,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         for (int j = 0; j < QH; ++j) {
             float s = 0.0f;
 #pragma unroll
-            for (int k = 0; k < D / 64; ++k) s = fmaf(qs[j * D + lane + 64 * k], kv[k], s);
+            for (int k = 0; k < D / 64; ++k) s = fmaf(qr[j][k], kv[k], s);
             s = wave_sum(s);
             if (lane == 0) rs[j * RS + i] = s;
         }
@@ -304,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 #pragma unroll
         for (int j = 0; j < QH; ++j) sc[s][j] = -INFINITY;
         if (step_ok(s)) {
-            const uint4(&cw)[NCH] = ring[s % NSLOT];
+            const u32x4(&cw)[NCH] = ring[s % NSLOT];
             float acc[QH][4];
 #pragma unroll
             for (int j = 0; j < QH; ++j)
@@ -403,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     for (int s = RW; s < 2 * RW; ++s) {
         issue(ring[(s + P) % NSLOT], s + P);
         if (step_ok(s) && step_tile(s) * kTileTokens + lane < t1) {
-            const uint4(&cw)[NCH] = ring[s % NSLOT];
+            const u32x4(&cw)[NCH] = ring[s % NSLOT];
             uint32_t p[QH];
 #pragma unroll
             for (int j = 0; j < QH; ++j) {
@@ -532,49 +587,48 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     }
     __syncthreads();
     if (!last_flag) return;
-    // Split maxima and sums to LDS (rs is free now), then every output element
-    // reads its n_split partial values with eight loads in flight.
+    // Every output element reads (max, sum, value) of eight splits at a time --
+    // all loads in flight together -- and folds them in with a running max.
     const float* prow0 = a.partials + (int64_t)(b * a.Hq + hq0) * a.n_split * a.pstride;
-    float* pm = rs;                       // [QH][n_split]
-    float* pl = rs + QH * a.n_split;      // [QH][n_split]
-    for (int e = tid; e < QH * a.n_split; e += kThreads) {
-        const int j = e / a.n_split;
-        const int sp = e - j * a.n_split;
-        const float* ps = prow0 + j * head_step + (int64_t)sp * a.pstride;
-        pm[e] = collect(ps + D);
-        pl[e] = collect(ps + D + 1);
-    }
-    __syncthreads();
     for (int e = tid; e < QH * D; e += kThreads) {
         const int j = e / D;
         const int el = e - j * D;
-        const float* pmj = pm + j * a.n_split;
-        const float* plj = pl + j * a.n_split;
-        float mall = -INFINITY;
-        for (int sp = 0; sp < a.n_split; ++sp) mall = fmaxf(mall, pmj[sp]);
+        const float* prow = prow0 + j * head_step;
+        float mall = -INFINITY, l = 0.0f, o = 0.0f;
+        for (int s0 = 0; s0 < a.n_split; s0 += 8) {
+            float pm[8], pl[8], po[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sp = s0 + u < a.n_split ? s0 + u : a.n_split - 1;
+                const float* ps = prow + (int64_t)sp * a.pstride;
+                pm[u] = collect(ps + D);
+                pl[u] = collect(ps + D + 1);
+                po[u] = collect(ps + el);
+            }
+            float cm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < a.n_split) cm = fmaxf(cm, pm[u]);
+            if (cm == -INFINITY) continue;
+            const float mnew = fmaxf(mall, cm);
+            const float r = exp2f(mall - mnew);  // 0 while nothing has been folded in
+            l *= r;
+            o *= r;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (s0 + u < a.n_split && pm[u] != -INFINITY) {
+                    const float wgt = exp2f(pm[u] - mnew);
+                    l = fmaf(wgt, pl[u], l);
+                    o = fmaf(wgt, po[u], o);
+                }
+            }
+            mall = mnew;
+        }
         const int64_t orow = (int64_t)(b * a.Hq + hq0 + j);
         if (mall == -INFINITY) {
             a.out[orow * D + el] = 0.0f;
             if (el == 0) a.lse[orow] = -INFINITY;
             continue;
-        }
-        const float* pe = prow0 + j * head_step + el;
-        float l = 0.0f, o = 0.0f;
-        for (int s0 = 0; s0 < a.n_split; s0 += 8) {
-            float v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int sp = s0 + u < a.n_split ? s0 + u : a.n_split - 1;
-                v[u] = collect(pe + (int64_t)sp * a.pstride);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (s0 + u < a.n_split && pmj[s0 + u] != -INFINITY) {
-                    const float wgt = exp2f(pmj[s0 + u] - mall);
-                    l = fmaf(wgt, plj[s0 + u], l);
-                    o = fmaf(wgt, v[u], o);
-                }
-            }
         }
         a.out[orow * D + el] = o / l;
         if (el == 0) a.lse[orow] = (mall + log2f(l)) * kLn2;
@@ -618,11 +672,9 @@ hipError_t launch_typed(const pqkv_dims& d, int32_t batch, const DecodePlan& pla
     k.pstride = plan.partial_stride;
     k.split_tokens = plan.split_tokens;
     const int64_t items = (int64_t)batch * d.n_kv_heads * plan.n_groups * plan.n_split;
-    const int64_t per_xcd = (items + 7) / 8;
     k.n_items = (int)items;
-    k.per_xcd = (int)per_xcd;
-    hipLaunchKernelGGL((pq_decode_kernel<M, DSUB, QH, QT, RT>), dim3((unsigned)(per_xcd * 8)), dim3(kThreads), 0,
-                       stream, k);
+    hipLaunchKernelGGL((pq_decode_kernel<M, DSUB, QH, QT, RT>), dim3((unsigned)items), dim3(kThreads), 0, stream,
+                       k);
     return hipGetLastError();
 }
 
