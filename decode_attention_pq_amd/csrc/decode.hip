@@ -177,6 +177,8 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     constexpr int LUT_PER_THREAD = kLdsRows * M / kThreads;  // (centroid, subspace) pairs per thread
     constexpr int CPL = D / 64;                // epilogue: output components per lane
     constexpr int CPER = kLdsRows / kWaves;    // epilogue: centroids per wave
+    constexpr int CHALF = CPER / 2;            // of which staged through LDS
+    static_assert(kWaves * CHALF * D <= kLdsRows * kRow, "staged value rows must fit the LUT region");
     static_assert(QH * M <= kRow, "query-head group must fit one LDS row");
 
     // LDS: histogram (u32) at byte 0, LUT at byte 65536, then the small buffers.
@@ -420,17 +422,31 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     // ---- 5. phase 2: add round(p * 2^S) into histogram[code][m].
     // First request this thread's value-codebook entries for the epilogue: lane
     // (cg, m) of wave w covers subspace m, components [cg*CPL, cg*CPL + CPL) and
-    // centroids [w*CPER, w*CPER + CPER).
+    // centroids [w*CPER, w*CPER + CPER).  The first half of those centroid rows
+    // go straight into this wave's 8 KiB block of the LUT region (unused from
+    // here on) with direct-to-LDS loads; the second half come to registers.
     const int em = lane % M;
     const int ecomp = (lane / M) * CPL;
     const int ec0 = wave * CPER;
+    float* cv_lds = lds + kLdsRows * kRow + wave * (CHALF * D);
+    {
+        const float* head = a.cb_v ? a.cb_v + (int64_t)h * K * D : nullptr;
+#pragma unroll
+        for (int i = 0; i < CHALF * D / 256; ++i) {  // 1 KiB (64 lanes x 16 bytes) per load
+            const int foff = ec0 * D + i * 256 + lane * 4;
+            const float* src = (head && foff / D < K) ? head + foff
+                                                      : reinterpret_cast<const float*>(g_zero_block) + lane * 4;
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(cv_lds + i * 256), 16,
+                                             0, 0);
+        }
+    }
     const float* cbv = a.cb_v ? a.cb_v + (int64_t)h * K * M * DSUB + em * DSUB + ecomp
                               : reinterpret_cast<const float*>(g_zero_block);
     const int vstride = a.cb_v ? M * DSUB : 0;
-    float cvr[CPER][CPL];
+    float cvr[CPER - CHALF][CPL];
 #pragma unroll
-    for (int k = 0; k < CPER; ++k) {
-        const int c = ec0 + k < K ? ec0 + k : K - 1;
+    for (int k = 0; k < CPER - CHALF; ++k) {
+        const int c = ec0 + CHALF + k < K ? ec0 + CHALF + k : K - 1;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) cvr[k][i] = cbv[(int64_t)c * vstride + i];
     }
@@ -516,14 +532,33 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
             for (int i = 0; i < CPL; ++i) acc[j][i] = 0.0f;
         if (any) {
             if (has_hist) {
+                // the staged value-codebook rows must have landed in LDS
+                __builtin_amdgcn_s_waitcnt(0);
+                __builtin_amdgcn_sched_barrier(0);
+                // histogram reads in groups of 8 (rows past K read a valid row and count
+                // 0), so the LDS latency is paid once per group
 #pragma unroll
-                for (int k = 0; k < CPER; ++k) {
-                    if (ec0 + k < K) {
+                for (int k0 = 0; k0 < CPER; k0 += 8) {
+                    uint32_t hv[8][QH];
+                    float cv[8][CPL];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const int c = ec0 + k0 + k < K ? ec0 + k0 + k : K - 1;
+#pragma unroll
+                        for (int j = 0; j < QH; ++j) hv[k][j] = hist[c * kRow + j * M + em];
+#pragma unroll
+                        for (int i = 0; i < CPL; ++i)
+                            cv[k][i] = k0 + k < CHALF ? cv_lds[(k0 + k) * D + em * DSUB + ecomp + i]
+                                                      : cvr[k0 + k - CHALF < 0 ? 0 : k0 + k - CHALF][i];
+                    }
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const bool live = ec0 + k0 + k < K;
 #pragma unroll
                         for (int j = 0; j < QH; ++j) {
-                            const float hv = (float)hist[(ec0 + k) * kRow + j * M + em];
+                            const float w = live ? (float)hv[k][j] : 0.0f;
 #pragma unroll
-                            for (int i = 0; i < CPL; ++i) acc[j][i] = fmaf(hv, cvr[k][i], acc[j][i]);
+                            for (int i = 0; i < CPL; ++i) acc[j][i] = fmaf(w, cv[k][i], acc[j][i]);
                         }
                     }
                 }
