@@ -55,22 +55,79 @@ constexpr int kRecentPre = 4; // recent rows per wave requested before the first
 __device__ inline float to_f32(float v) { return v; }
 __device__ inline float to_f32(__half v) { return __half2float(v); }
 
+// Wave-wide reductions on DPP lane moves (no LDS round trips): pairs, quads,
+// half rows and rows of 16 by quad permutes and mirrors, then rows 0+1 and 2+3
+// by row_bcast:15 and the whole wave by row_bcast:31; lane 63 ends with the
+// total, which readlane makes uniform.  Lanes a row-masked move does not write
+// take `id`, the operation's identity.
+template <int CTRL, int ROWS>
+__device__ inline uint32_t dpp_move(uint32_t v, uint32_t id) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+template <typename Op>
+__device__ inline uint32_t wave_reduce(uint32_t v, uint32_t id, Op op) {
+    v = op(v, dpp_move<0xB1, 0xF>(v, id));   // quad_perm [1,0,3,2]
+    v = op(v, dpp_move<0x4E, 0xF>(v, id));   // quad_perm [2,3,0,1]
+    v = op(v, dpp_move<0x141, 0xF>(v, id));  // row_half_mirror
+    v = op(v, dpp_move<0x140, 0xF>(v, id));  // row_mirror
+    v = op(v, dpp_move<0x142, 0xA>(v, id));  // row_bcast:15 into rows 1 and 3
+    v = op(v, dpp_move<0x143, 0xC>(v, id));  // row_bcast:31 into rows 2 and 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 __device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    return __uint_as_float(wave_reduce(__float_as_uint(v), 0xff800000u, [](uint32_t x, uint32_t y) {
+        return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+    }));
 }
 
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    return __uint_as_float(wave_reduce(__float_as_uint(v), 0u, [](uint32_t x, uint32_t y) {
+        return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+    }));
 }
 
 __device__ inline uint32_t wave_sum_u32(uint32_t v) {
+    return wave_reduce(v, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+}
+
+// LDS byte offset of a pointer into a __shared__ array.
+__device__ inline uint32_t lds_offset(const float* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)p;
+}
+
+// Direct-to-LDS 16-byte load: lane l's 16 bytes from `src` land at LDS byte
+// `lds_base + 16*l` (lds_base wave-uniform).  Issued from inline assembly so
+// the compiler does not make every later LDS access wait for all outstanding
+// loads; the reader must wait (vmcnt 0) before touching the destination.  M0,
+// which holds the LDS base for the instruction, is restored afterwards.
+__device__ inline void lds_dma16(const void* src, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+        : "memory");
+}
+
+// N consecutive floats (N = 2 or 4, 8- or 16-byte aligned) in one load.
+template <int N>
+__device__ inline void load_f32x(const float* p, float (&v)[N]) {
+    if constexpr (N == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(p);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else if constexpr (N == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(p);
+        v[0] = t.x; v[1] = t.y;
+    } else {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+        for (int i = 0; i < N; ++i) v[i] = p[i];
+    }
 }
 
 // Histogram byte address of byte s of code word `cw`, with byte s of offset word
@@ -239,6 +296,11 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 #pragma unroll
         for (int k = 0; k < D / 64; ++k) qr[j][k] = to_f32(qrow[j * D + lane + 64 * k]);
     }
+    // The splits of one head share an L2: each starts on a different block of
+    // centroids, so the first requests of all of them together cover the
+    // codebook once and the later ones find it in L2.
+    const int lut_rot = split * LUT_LOADS / (a.n_split < LUT_LOADS ? a.n_split : LUT_LOADS);
+    auto lut_block = [&](int k) { return (k + lut_rot) % LUT_LOADS; };
     float4 cbq[LUT_LOADS];
     {
         const float* cbh = a.cb_k ? a.cb_k + (int64_t)h * K * M * DSUB + mg * 4
@@ -246,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         const int cstride = a.cb_k ? M * DSUB : 0;
 #pragma unroll
         for (int k = 0; k < LUT_LOADS; ++k) {
-            int c = (tid + k * kThreads) / (M / EPL);
+            int c = (tid + lut_block(k) * kThreads) / (M / EPL);
             c = c < K ? c : K - 1;
             cbq[k] = *reinterpret_cast<const float4*>(cbh + (int64_t)c * cstride);
         }
@@ -307,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     if (has_hist) {
 #pragma unroll
         for (int k = 0; k < LUT_LOADS; ++k) {
-            const int c = (tid + k * kThreads) / (M / EPL);
+            const int c = (tid + lut_block(k) * kThreads) / (M / EPL);
             if (c < K) {
                 const float cv[4] = {cbq[k].x, cbq[k].y, cbq[k].z, cbq[k].w};
 #pragma unroll
@@ -423,21 +485,21 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     // First request this thread's value-codebook entries for the epilogue: lane
     // (cg, m) of wave w covers subspace m, components [cg*CPL, cg*CPL + CPL) and
     // centroids [w*CPER, w*CPER + CPER).  The first half of those centroid rows
-    // go straight into this wave's 8 KiB block of the LUT region (unused from
-    // here on) with direct-to-LDS loads; the second half come to registers.
+    // go straight into this wave's block of the LUT region (unused from here on)
+    // by direct-to-LDS loads; the second half come to registers.
     const int em = lane % M;
     const int ecomp = (lane / M) * CPL;
     const int ec0 = wave * CPER;
-    float* cv_lds = lds + kLdsRows * kRow + wave * (CHALF * D);
+    const float* cv_lds = lds + kLdsRows * kRow + wave * (CHALF * D);
     {
         const float* head = a.cb_v ? a.cb_v + (int64_t)h * K * D : nullptr;
+        const uint32_t dst = lds_offset(cv_lds);
 #pragma unroll
         for (int i = 0; i < CHALF * D / 256; ++i) {  // 1 KiB (64 lanes x 16 bytes) per load
             const int foff = ec0 * D + i * 256 + lane * 4;
             const float* src = (head && foff / D < K) ? head + foff
                                                       : reinterpret_cast<const float*>(g_zero_block) + lane * 4;
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(cv_lds + i * 256), 16,
-                                             0, 0);
+            lds_dma16(src, dst + i * 1024);
         }
     }
     const float* cbv = a.cb_v ? a.cb_v + (int64_t)h * K * M * DSUB + em * DSUB + ecomp
@@ -447,8 +509,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int k = 0; k < CPER - CHALF; ++k) {
         const int c = ec0 + CHALF + k < K ? ec0 + CHALF + k : K - 1;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) cvr[k][i] = cbv[(int64_t)c * vstride + i];
+        load_f32x<CPL>(cbv + (int64_t)c * vstride, cvr[k]);
     }
     float vpre[kRecentPre][CPL];  // recent value rows of this wave's first recent tokens
 #pragma unroll
@@ -532,7 +593,8 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
             for (int i = 0; i < CPL; ++i) acc[j][i] = 0.0f;
         if (any) {
             if (has_hist) {
-                // the staged value-codebook rows must have landed in LDS
+                // the staged value-codebook rows must have landed in LDS (the
+                // direct-to-LDS loads are not tracked by the compiler's waits)
                 __builtin_amdgcn_s_waitcnt(0);
                 __builtin_amdgcn_sched_barrier(0);
                 // histogram reads in groups of 8 (rows past K read a valid row and count
