@@ -75,7 +75,8 @@ def measured_traffic(workload: str):
 
 
 def algorithmic_bytes(w, r_len):
-    """Bytes the method itself must move for one decode call (per-unit figures)."""
+    """Bytes the method itself must move for one decode call: 2*M per history token and kv head for the
+    codes, fp16 K and V per recent token, fp32 K and V codebooks per kv head, q in and out + lse out."""
     M = w.n_sub
     T = sum(w.hist_len)
     codes = 2 * M * T * w.n_kv_heads                       # K and V codes, 2*M per history token per kv head
