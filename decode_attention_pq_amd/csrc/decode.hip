@@ -200,18 +200,22 @@ __device__ inline void load4(const __half* p, float (&v)[4]) {
 }
 
 struct DecArgs {
+    // first 64 bytes: everything the work mapping and the first loads need, so one
+    // scalar load brings it in
+    int K, Hq, Hkv, n_groups, n_split, rounds, pstride, n_items;
+    int64_t split_tokens;
+    const int32_t* hist_len;
+    const int32_t* recent_len;
     const void* q;
     const float* cb_k;
     const float* cb_v;
     const uint8_t* codes_k;
     const uint8_t* codes_v;
     int64_t t_cap;
-    const int32_t* hist_len;
     int64_t max_hist;
     const void* rk;
     const void* rv;
     int64_t r_cap;
-    const int32_t* recent_len;
     float scale_log2;
     float fix_scale;  // 2^S
     float fix_inv;    // 2^-S
@@ -219,8 +223,6 @@ struct DecArgs {
     uint32_t* counters;
     float* out;
     float* lse;
-    int K, Hq, Hkv, n_groups, n_split, rounds, pstride, n_items;
-    int64_t split_tokens;
 };
 
 template <int M, int DSUB, int QH, typename QT, typename RT>
@@ -270,11 +272,10 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     // The lengths come through the vector memory path: scalar loads return out of
     // order, so waiting for one would also wait for every later scalar load.  They
     // are used only after the length-independent loads below have been issued.
-    const int T_in = __hip_atomic_load(const_cast<int32_t*>(a.hist_len + b), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-    const int R_in = a.recent_len ? __hip_atomic_load(const_cast<int32_t*>(a.recent_len + b), __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT)
-                                  : 0;
+    int len_idx = b;
+    asm volatile("" : "+v"(len_idx));  // a per-lane index makes these vector loads
+    const int T_in = a.hist_len[len_idx];
+    const int R_in = a.recent_len ? a.recent_len[len_idx] : 0;
     const int64_t t0 = (int64_t)split * a.split_tokens;
     const int64_t tile0 = t0 / kTileTokens;
     const int rounds = a.rounds;
