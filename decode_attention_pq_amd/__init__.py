@@ -15,7 +15,7 @@ import torch  # loads the HIP runtime libpqkv.so binds to (same soname)
 
 __all__ = [
     "PQKVError", "Dims", "lib", "LIB_PATH", "encode", "build_lut", "decode_workspace_bytes",
-    "decode_attention", "merge", "code_plane_bytes", "F16", "F32", "MAX_RECENT", "TILE_TOKENS",
+    "decode_attention", "append_kv", "merge", "code_plane_bytes", "F16", "F32", "MAX_RECENT", "TILE_TOKENS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpqkv.so")
@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.pqkv_decode_attention.argtypes = [dp, i32, vp, i32, vp, vp, vp, vp, i64, vp, i64, vp, vp, i32, i64,
                                             vp, f32, vp, vp, vp, sz, vp]
         L.pqkv_decode_attention.restype = i32
+        L.pqkv_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                                     i64, i64, vp]
+        L.pqkv_append_kv.restype = i32
         L.pqkv_merge.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp]
         L.pqkv_merge.restype = i32
         L.pqkv_status_str.argtypes = [i32]
@@ -169,6 +172,30 @@ def decode_attention(dims: Dims, q, codebook_k, codebook_v, codes_k, codes_v, t_
         ctypes.byref(dims), B, _ptr(q), _dtype_code(q), _ptr(codebook_k), _ptr(codebook_v), _ptr(codes_k),
         _ptr(codes_v), t_cap, _ptr(hist_len), max_hist_len, _ptr(recent_k), _ptr(recent_v), rdt, r_cap,
         _ptr(recent_len), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream()))
+
+
+def append_kv(dims: Dims, new_k, new_v, recent_k, recent_v, hist_len_in, recent_len_in, hist_len_out,
+              recent_len_out, n_roll: int, codebook_k, codebook_v, codes_k, codes_v, t_cap: int,
+              max_hist_len: int) -> None:
+    """pqkv_append_kv.  new_k/v: [B, Hkv, d]; recent_k/v: [B, Hkv, r_cap, d] (same dtype, updated in
+    place); *_len_in / *_len_out: int32 [B] (device, out distinct from in); codes_k/v: uint8
+    [B, Hkv, t_cap*M] (updated in place)."""
+    _dev(new_k, new_v, recent_k, recent_v, hist_len_in, recent_len_in, hist_len_out, recent_len_out,
+         codebook_k, codebook_v, codes_k, codes_v)
+    B = new_k.shape[0]
+    for t in (new_k, new_v, recent_k, recent_v, codebook_k, codebook_v, codes_k, codes_v):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    for t in (hist_len_in, recent_len_in, hist_len_out, recent_len_out):
+        if t.dtype != torch.int32:
+            raise ValueError("lengths must be int32")
+    if not (new_k.dtype == new_v.dtype == recent_k.dtype == recent_v.dtype):
+        raise ValueError("new and recent rows must share one dtype")
+    _check("pqkv_append_kv", lib().pqkv_append_kv(
+        ctypes.byref(dims), B, _ptr(new_k), _ptr(new_v), _ptr(recent_k), _ptr(recent_v), _dtype_code(recent_k),
+        recent_k.shape[2], _ptr(hist_len_in), _ptr(recent_len_in), _ptr(hist_len_out), _ptr(recent_len_out),
+        n_roll, _ptr(codebook_k), _ptr(codebook_v), _ptr(codes_k), _ptr(codes_v), t_cap, max_hist_len,
+        _stream()))
 
 
 def merge(out_a, lse_a, out_b, lse_b, out, lse) -> None:

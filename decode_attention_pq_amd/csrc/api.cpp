@@ -40,6 +40,12 @@ pqkv_status check_dims(const pqkv_dims* d) {
 
 pqkv_status hip_status(hipError_t e) { return e == hipSuccess ? PQKV_OK : PQKV_ERR_HIP; }
 
+// Byte ranges [a, a + n) and [b, b + n) overlap.
+bool overlap(const void* a, const void* b, size_t n) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + n && y < x + n;
+}
+
 }  // namespace
 
 DecodePlan plan_decode(const pqkv_dims& d, int32_t batch, int64_t max_hist_len) {
@@ -196,6 +202,39 @@ pqkv_status pqkv_merge(int64_t n_rows, int32_t head_dim, const float* out_a, con
     if (!out_a || !lse_a || !out_b || !lse_b || !out || !lse) return PQKV_ERR_INVALID;
     if ((n_rows + 3) / 4 > 0x7fffffffLL) return PQKV_ERR_UNSUPPORTED;
     return hip_status(launch_merge_states(n_rows, head_dim, out_a, lse_a, out_b, lse_b, out, lse, stream));
+}
+
+pqkv_status pqkv_append_kv(const pqkv_dims* dims, int32_t batch, const void* new_k, const void* new_v,
+                           void* recent_k, void* recent_v, pqkv_dtype recent_dtype, int64_t r_cap,
+                           const int32_t* hist_len_in, const int32_t* recent_len_in, int32_t* hist_len_out,
+                           int32_t* recent_len_out, int32_t n_roll, const float* codebook_k,
+                           const float* codebook_v, uint8_t* codes_k, uint8_t* codes_v, int64_t t_cap,
+                           int64_t max_hist_len, hipStream_t stream) {
+    const pqkv_status ds = check_dims(dims);
+    if (ds != PQKV_OK) return ds;
+    if (!dtype_ok(recent_dtype)) return PQKV_ERR_INVALID;
+    if (batch < 0 || r_cap < 1 || n_roll < 1 || n_roll > r_cap || max_hist_len < 0) return PQKV_ERR_INVALID;
+    if (t_cap <= 0 || t_cap % kTileTokens || max_hist_len + n_roll > t_cap) return PQKV_ERR_INVALID;
+    if (r_cap > PQKV_MAX_RECENT || n_roll > 512 || batch > 65535) return PQKV_ERR_UNSUPPORTED;
+    if (batch == 0) return PQKV_OK;
+    if (!new_k || !new_v || !recent_k || !recent_v || !hist_len_in || !recent_len_in || !hist_len_out ||
+        !recent_len_out || !codebook_k || !codebook_v || !codes_k || !codes_v)
+        return PQKV_ERR_INVALID;
+    // rows move with 16-byte loads and stores
+    if (!aligned(new_k, 16) || !aligned(new_v, 16) || !aligned(recent_k, 16) || !aligned(recent_v, 16) ||
+        !aligned(codebook_k, 16) || !aligned(codebook_v, 16))
+        return PQKV_ERR_INVALID;
+    // every work-group reads the old lengths while one per sequence writes the new ones
+    const size_t lb = (size_t)batch * sizeof(int32_t);
+    const void* ins[2] = {hist_len_in, recent_len_in};
+    const void* outs[2] = {hist_len_out, recent_len_out};
+    for (const void* o : outs)
+        for (const void* i : ins)
+            if (overlap(o, i, lb)) return PQKV_ERR_INVALID;
+    if (overlap(hist_len_out, recent_len_out, lb)) return PQKV_ERR_INVALID;
+    return hip_status(launch_append(*dims, batch, new_k, new_v, recent_k, recent_v, recent_dtype, r_cap,
+                                    hist_len_in, recent_len_in, hist_len_out, recent_len_out, n_roll,
+                                    codebook_k, codebook_v, codes_k, codes_v, t_cap, stream));
 }
 
 }  // extern "C"

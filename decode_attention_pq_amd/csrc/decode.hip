@@ -534,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     for (int j = 0; j < QH; ++j) lsum[j] = 0u;
 #pragma unroll
     for (int s = RW; s < 2 * RW; ++s) {
-        issue(ring[(s + P) % NSLOT], s + P);
+        if (s + P < 2 * RW) issue(ring[(s + P) % NSLOT], s + P);  // nothing is left to request at the end
         if (step_ok(s) && step_tile(s) * kTileTokens + lane < t1) {
             const u32x4(&cw)[NCH] = ring[s % NSLOT];
             uint32_t p[QH];

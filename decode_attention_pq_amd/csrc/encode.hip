@@ -13,53 +13,12 @@
 // same time, so the LDS reads are broadcasts.  The scan is plain fp32 VALU work:
 // (x - c)^2 summed over the subspace, strict '<' in ascending centroid order.
 
-#include <hip/hip_fp16.h>
-
-#include "pqkv_internal.h"
+#include "nearest.h"
 
 namespace pqkv {
 namespace {
 
 constexpr int kEncThreads = 512;
-
-template <typename T>
-struct Row;
-
-template <>
-struct Row<float> {
-    template <int D>
-    __device__ static void load(const float* __restrict__ p, float (&v)[D]) {
-        const float4* p4 = reinterpret_cast<const float4*>(p);
-#pragma unroll
-        for (int i = 0; i < D / 4; ++i) {
-            float4 t = p4[i];
-            v[4 * i + 0] = t.x;
-            v[4 * i + 1] = t.y;
-            v[4 * i + 2] = t.z;
-            v[4 * i + 3] = t.w;
-        }
-    }
-};
-
-template <>
-struct Row<__half> {
-    template <int D>
-    __device__ static void load(const __half* __restrict__ p, float (&v)[D]) {
-        const uint4* p4 = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-        for (int i = 0; i < D / 8; ++i) {
-            uint4 t = p4[i];
-            const uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                __half2 h2 = *reinterpret_cast<const __half2*>(&w[k]);
-                float2 f = __half22float2(h2);
-                v[8 * i + 2 * k + 0] = f.x;
-                v[8 * i + 2 * k + 1] = f.y;
-            }
-        }
-    }
-};
 
 template <int D, int DSUB, typename XT>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(
@@ -83,31 +42,8 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     Row<XT>::template load<D>(x + b * s_seq + i * s_tok + h * s_head, xv);
 
     const int64_t t = t_start + i;
-    const int slot = (int)(t & (kTileTokens - 1));
-    uint8_t* dst = codes + ((int64_t)b * Hkv + h) * t_cap * M + (t >> 6) * (kTileTokens * M) + slot * 16;
-
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        float best = INFINITY;
-        int bi = 0;
-        const float* cm = cbs + m * DSUB;
-#pragma unroll 4
-        for (int c = 0; c < K; ++c) {
-            const float* cc = cm + c * D;
-            float dd = 0.0f;
-#pragma unroll
-            for (int j = 0; j < DSUB; ++j) {
-                const float e = xv[m * DSUB + j] - cc[j];
-                dd = fmaf(e, e, dd);
-            }
-            if (dd < best) {
-                best = dd;
-                bi = c;
-            }
-        }
-        const int p = (m - slot) & (M - 1);
-        dst[(p >> 4) * (kTileTokens * 16) + (p & 15)] = (uint8_t)bi;
-    }
+    write_nearest_codes<D, DSUB>(xv, cbs, K, code_slot<M>(codes + ((int64_t)b * Hkv + h) * t_cap * M, t),
+                                 (int)(t & (kTileTokens - 1)));
 }
 
 template <int D, int DSUB, typename XT>

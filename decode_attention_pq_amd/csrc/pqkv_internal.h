@@ -70,6 +70,12 @@ struct DecodeArgs {
 hipError_t launch_decode(const pqkv_dims& d, int32_t batch, pqkv_dtype qt, pqkv_dtype rt,
                          const DecodePlan& plan, const DecodeArgs& a, hipStream_t stream);
 
+hipError_t launch_append(const pqkv_dims& d, int32_t batch, const void* new_k, const void* new_v,
+                         void* recent_k, void* recent_v, pqkv_dtype rt, int64_t r_cap,
+                         const int32_t* hist_in, const int32_t* recent_in, int32_t* hist_out,
+                         int32_t* recent_out, int32_t n_roll, const float* cb_k, const float* cb_v,
+                         uint8_t* codes_k, uint8_t* codes_v, int64_t t_cap, hipStream_t stream);
+
 hipError_t launch_merge_states(int64_t n_rows, int32_t head_dim, const float* out_a,
                                const float* lse_a, const float* out_b, const float* lse_b,
                                float* out, float* lse, hipStream_t stream);

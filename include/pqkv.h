@@ -171,6 +171,49 @@ pqkv_status pqkv_decode_attention(const pqkv_dims* dims, int32_t batch, const vo
                                   hipStream_t stream);
 
 /*
+ * pqkv_append_kv -- one decode step of the live cache: each sequence's new key
+ * and value enter its recent full-precision window, and a window that is full
+ * first rolls its oldest n_roll tokens into the PQ history.  This is the batched,
+ * delayed quantisation of the Fig. 7 paragraph: generated tokens are kept in full
+ * precision, apart from the quantised history, and quantised later in batches.
+ *
+ * For every sequence b, with T = hist_len_in[b] and R = recent_len_in[b]:
+ *   1. if R == r_cap: for every kv head h, rows 0..n_roll-1 of recent_k/v[b][h] are
+ *      encoded exactly as pqkv_encode would (same codes, same tie rule) into history
+ *      positions T..T+n_roll-1 of planes (b, h) of codes_k/v; rows n_roll..R-1 move
+ *      down to rows 0..R-n_roll-1; T += n_roll; R -= n_roll;
+ *   2. new_k/v[b][h] is written to recent row R of every head, and R += 1;
+ *   3. hist_len_out[b] = T, recent_len_out[b] = R.
+ * So hist_len + recent_len grows by exactly one per call, and the recent window
+ * always holds the newest tokens in order.  Rows and code bytes of other
+ * positions are left untouched.
+ *
+ *   new_k/new_v     device [batch][Hkv][d] in recent_dtype, dense, 16-byte aligned.
+ *   recent_k/v      device [batch][Hkv][r_cap][d] in recent_dtype, dense, 16-byte aligned;
+ *                   updated in place.
+ *   r_cap           1..PQKV_MAX_RECENT;  n_roll in 1..min(r_cap, 512).
+ *   hist_len_in, recent_len_in    device int32 [batch]: 0 <= hist_len_in[b] <= max_hist_len,
+ *                   0 <= recent_len_in[b] <= r_cap.
+ *   hist_len_out, recent_len_out  device int32 [batch]; must not overlap each other or the
+ *                   _in arrays (every work-group reads the old lengths while one per
+ *                   sequence writes the new ones); swap in and out between steps.
+ *   codebook_k/v    device fp32 [Hkv][K][M][d_sub], 16-byte aligned.
+ *   codes_k/v       device uint8 cache planes (layout above), updated in place.
+ *   t_cap           plane capacity in tokens, multiple of 64, max_hist_len + n_roll <= t_cap.
+ *   max_hist_len    host bound on hist_len_in (as for pqkv_decode_attention).
+ * A sequence whose device lengths break these bounds is left unchanged and its
+ * out lengths repeat the in lengths.  Errors: INVALID for null pointers, bad
+ * sizes or alignment, overlapping length arrays, bad dtype; UNSUPPORTED for dims
+ * outside the ranges above, r_cap > PQKV_MAX_RECENT, n_roll > 512 or batch > 65535.
+ */
+pqkv_status pqkv_append_kv(const pqkv_dims* dims, int32_t batch, const void* new_k, const void* new_v,
+                           void* recent_k, void* recent_v, pqkv_dtype recent_dtype, int64_t r_cap,
+                           const int32_t* hist_len_in, const int32_t* recent_len_in, int32_t* hist_len_out,
+                           int32_t* recent_len_out, int32_t n_roll, const float* codebook_k,
+                           const float* codebook_v, uint8_t* codes_k, uint8_t* codes_v, int64_t t_cap,
+                           int64_t max_hist_len, hipStream_t stream);
+
+/*
  * pqkv_merge -- log-sum-exp merge of two normalised attention states over
  * disjoint token sets (the combination step of the Fig. 7 paragraph):
  *     mu = max(lse_a, lse_b),  wa = exp(lse_a - mu),  wb = exp(lse_b - mu),

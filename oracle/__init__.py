@@ -28,6 +28,11 @@ write-up) states it:
   softmax partials (flash decoding, Fig. 8 paragraph) and a log-sum-exp merge.
 * O6  ``compression_ratio`` and friends -- byte accounting (4x at d_sub=2 with
   8-bit codes versus fp16, stated in the LongBench and TPOT paragraphs).
+* O7  ``append_kv_step`` -- one step of the live cache (Fig. 7 paragraph:
+  generated tokens are kept in full precision, apart from the quantised
+  history, and quantised later in batches): a full recent window first moves
+  its oldest tokens, encoded by O2, to the end of the history; the new token
+  then joins the window.
 * ``code_offsets`` / ``tile_codes`` / ``untile_codes`` -- the code-cache byte
   layout the C interface defines (a format, implemented here on its own from
   its definition).
@@ -352,6 +357,30 @@ def decode_method(q, cb_k, cb_v, codes_k, codes_v, hist_len, recent_k, recent_v,
 # ---------------------------------------------------------------- code-cache layout
 TILE_TOKENS = 64
 CHUNK_BYTES = 16
+
+
+def append_kv_step(state, new_k, new_v, cb_k, cb_v, r_cap: int, n_roll: int):
+    """One decode step of the live cache, per sequence b (Fig. 7 paragraph).
+
+    state: dict of per-sequence lists --
+      'codes_k', 'codes_v': uint8 [T_b, H, M] history codes;
+      'amb_k', 'amb_v':     bool  [T_b, H, M], True where the code's runner-up is within the
+                            encode ambiguity band (always False for codes given at the start);
+      'recent_k', 'recent_v': [R_b, H, d] full-precision recent rows, oldest first.
+    new_k, new_v: [B, H, d].  If R_b == r_cap, rows [0, n_roll) are encoded (O2) and appended to
+    the history and the window keeps rows [n_roll, R_b); then the new row is appended to the
+    window.  Returns a new state dict (inputs are not modified)."""
+    out = {k: list(v) for k, v in state.items()}
+    for b in range(len(out["recent_k"])):
+        for t_name, cb, new in (("k", cb_k, new_k), ("v", cb_v, new_v)):
+            rec = out["recent_" + t_name][b]
+            if rec.shape[0] == r_cap:
+                codes, _, _, amb = encode(rec[:n_roll], cb)
+                out["codes_" + t_name][b] = np.concatenate([out["codes_" + t_name][b], codes], axis=0)
+                out["amb_" + t_name][b] = np.concatenate([out["amb_" + t_name][b], amb], axis=0)
+                rec = rec[n_roll:]
+            out["recent_" + t_name][b] = np.concatenate([rec, np.asarray(new[b])[None]], axis=0)
+    return out
 
 
 def code_offsets(n_sub: int, t_cap: int) -> np.ndarray:

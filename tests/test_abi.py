@@ -24,7 +24,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(P):
     names = _declared()
-    assert {"pqkv_encode", "pqkv_build_lut", "pqkv_decode_attention", "pqkv_merge",
+    assert {"pqkv_encode", "pqkv_build_lut", "pqkv_decode_attention", "pqkv_merge", "pqkv_append_kv",
             "pqkv_decode_workspace_bytes", "pqkv_status_str"} <= set(names)
     for n in names:
         assert hasattr(P.lib(), n), n
@@ -111,6 +111,30 @@ def test_merge_validation(P):
     assert L.pqkv_merge(4, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
     assert L.pqkv_merge(0, 128, None, None, None, None, None, None, None) == 0
     assert L.pqkv_merge(4, 128, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_append_validation(P):
+    L = P.lib()
+    F2, F3, F4, F5 = (ctypes.c_void_p(0x20000 + 0x1000 * i) for i in range(4))  # distinct length arrays
+
+    def call(dims=(128, 2, 256, 32, 32), batch=2, r_cap=128, n_roll=64, t_cap=4096, max_hist=1000,
+             hin=F2, rin=F3, hout=F4, rout=F5, dt=0, new_k=FAKE, rk=FAKE, cb=FAKE):
+        return L.pqkv_append_kv(_d(P, *dims), batch, new_k, FAKE, rk, FAKE, dt, r_cap, hin, rin, hout, rout,
+                                n_roll, cb, FAKE, FAKE, FAKE, t_cap, max_hist, None)
+
+    assert call(batch=0, new_k=None) == 0                  # nothing to do
+    assert call(dims=(96, 2, 256, 32, 32)) == 2            # head_dim unsupported
+    assert call(n_roll=0) == 1 and call(n_roll=129) == 1   # n_roll outside 1..r_cap
+    assert call(r_cap=2048, n_roll=600) == 2               # window and roll beyond the supported sizes
+    assert call(r_cap=0) == 1
+    assert call(t_cap=100) == 1                            # not a multiple of 64
+    assert call(max_hist=4090) == 1                        # a roll could pass the capacity
+    assert call(dt=5) == 1
+    assert call(new_k=None) == 1
+    assert call(rk=ctypes.c_void_p(0x10008)) == 1          # rows not 16-byte aligned
+    assert call(hout=F2) == 1 and call(rout=F3) == 1       # out lengths alias the in lengths
+    assert call(hout=ctypes.c_void_p(0x20004)) == 1        # out overlaps in by one element
+    assert call(rout=F4) == 1                              # the two out arrays overlap
 
 
 def test_product_path_does_not_touch_the_oracle():

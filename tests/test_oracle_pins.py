@@ -479,3 +479,46 @@ def test_generator_deterministic_and_shaped():
     assert synthkv.WORKLOADS["full32_ragged4"].hist_len == (14698, 3634, 31436, 30564)
     v = synthkv.kv_values(w, 0, "v", "history", 256)
     assert not np.array_equal(a, v)
+
+
+# ------------------------------------------------------------------ O7 live-cache step
+@pytest.mark.parametrize("r_cap,n_roll", [(5, 3), (4, 4), (3, 1)])
+def test_append_step_equals_bulk_quantisation(oracle_mod, r_cap, n_roll):
+    """Batched, delayed quantisation moves tokens, it does not change them: after
+    any number of steps the history is the starting codes followed by the
+    pure-Python nearest codes of the oldest appended tokens, in order, and the
+    window holds the newest ones.  How many tokens have rolled follows from the
+    window arithmetic alone (an integer simulation of the lengths)."""
+    B, H, d, dsub, K, steps = 2, 2, 8, 2, 8, 23
+    M = d // dsub
+    cbk = synthkv.small_normal(41, (H, K, M, dsub))
+    cbv = synthkv.small_normal(42, (H, K, M, dsub))
+    start_codes = [np.zeros((0, H, M), np.uint8), synthkv.small_codes(43, (4, H, M), K)]
+    start_rk = [synthkv.small_normal(44, (0, H, d)), synthkv.small_normal(45, (r_cap, H, d))]
+    start_rv = [synthkv.small_normal(46, (0, H, d)), synthkv.small_normal(47, (r_cap, H, d))]
+    state = {"codes_k": list(start_codes), "codes_v": list(start_codes),
+             "amb_k": [np.zeros(c.shape, bool) for c in start_codes],
+             "amb_v": [np.zeros(c.shape, bool) for c in start_codes],
+             "recent_k": list(start_rk), "recent_v": list(start_rv)}
+    new_k = synthkv.small_normal(48, (steps, B, H, d))
+    new_v = synthkv.small_normal(49, (steps, B, H, d))
+    for s in range(steps):
+        state = oracle.append_kv_step(state, new_k[s], new_v[s], cbk, cbv, r_cap, n_roll)
+    for b in range(B):
+        R, rolled = start_rk[b].shape[0], 0
+        for _ in range(steps):
+            if R == r_cap:
+                R, rolled = R - n_roll, rolled + n_roll
+            R += 1
+            assert R <= r_cap
+        for t_name, cb, start_r, new in (("k", cbk, start_rk, new_k), ("v", cbv, start_rv, new_v)):
+            tokens = np.concatenate([start_r[b], new[:, b]], axis=0)  # every row that entered the window
+            assert state["recent_" + t_name][b].shape[0] == R
+            np.testing.assert_array_equal(state["recent_" + t_name][b], tokens[rolled:])
+            codes = state["codes_" + t_name][b]
+            assert codes.shape[0] == start_codes[b].shape[0] + rolled
+            np.testing.assert_array_equal(codes[:start_codes[b].shape[0]], start_codes[b])
+            for h in range(H):
+                for m in range(M):
+                    want = _nearest_bruteforce(tokens[:rolled, h, m * dsub:(m + 1) * dsub], cb[h, :, m])
+                    np.testing.assert_array_equal(codes[start_codes[b].shape[0]:, h, m], want)
