@@ -116,16 +116,12 @@ def main():
     scale = float(np.float32(1.0 / math.sqrt(d)))
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
 
-    # ---- inputs (single sequence per workload row of this bench)
+    # ---- inputs
     t0 = time.time()
-    cbk = torch.from_numpy(synthkv.drawn_codebook(w, 0, "k")).to(dev)
-    cbv = torch.from_numpy(synthkv.drawn_codebook(w, 0, "v")).to(dev)
-    planes = {}
     enc_ms = {}
-    for tensor, cb in (("k", cbk), ("v", cbv)):
-        x = torch.stack([torch.from_numpy(synthkv.history_kv(w, 0, tensor, b)) for b in range(B)]).to(dev)
-        codes = torch.zeros((B, Hkv, t_cap * M), dtype=torch.uint8, device=dev)
-        P.encode(dims, x, cb, codes, t_cap)  # warm-up and the codes used below
+
+    def time_encode(x, cb, codes):
+        P.encode(dims, x, cb, codes, t_cap)  # warm-up (and the codes used below)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -133,33 +129,85 @@ def main():
             P.encode(dims, x, cb, codes, t_cap)
         e1.record()
         torch.cuda.synchronize()
-        enc_ms[tensor] = e0.elapsed_time(e1) / args.encode_reps
-        planes[tensor] = codes
-        del x
+        return e0.elapsed_time(e1) / args.encode_reps
+
+    hist_len = torch.tensor(w.hist_len, dtype=torch.int32, device=dev)
+    recent_len = torch.full((B,), R, dtype=torch.int32, device=dev)
+    copies = []
+    if w.n_layers == 1:
+        # the history's real codes, encoded from its synthetic values (and timed)
+        cbk = torch.from_numpy(synthkv.drawn_codebook(w, 0, "k")).to(dev)
+        cbv = torch.from_numpy(synthkv.drawn_codebook(w, 0, "v")).to(dev)
+        planes = {}
+        for tensor, cb in (("k", cbk), ("v", cbv)):
+            x = torch.stack([torch.from_numpy(synthkv.history_kv(w, 0, tensor, b)) for b in range(B)]).to(dev)
+            codes = torch.zeros((B, Hkv, t_cap * M), dtype=torch.uint8, device=dev)
+            enc_ms[tensor] = time_encode(x, cb, codes)
+            planes[tensor] = codes
+            del x
+        enc_tokens = B * T * 2  # K and V of every history token
+        q = torch.from_numpy(synthkv.queries(w)).to(dev)
+        rk = torch.from_numpy(synthkv.recent_kv(w, 0, "k")).to(dev)
+        rv = torch.from_numpy(synthkv.recent_kv(w, 0, "v")).to(dev)
+        # every input of a call is rotated, codebooks included, so no call finds its
+        # data in the caches the previous calls filled
+        for i in range(args.copies):
+            copies.append(dict(q=q.clone(), ck=planes["k"].clone(), cv=planes["v"].clone(), rk=rk.clone(),
+                               rv=rv.clone(), cbk=cbk.clone(), cbv=cbv.clone()))
+        del planes
+        calls_per_step = 1
+    else:
+        # one decode step of every layer; each layer has its own codebooks, query, recent
+        # window and codes.  The codes are uniform random bytes drawn on the device
+        # (decode time does not depend on their values; the full history's synthetic
+        # values would take hours to draw and encode on the host).  pq_encode is timed
+        # on one layer's prefill draw.
+        g = torch.Generator(device=dev).manual_seed(w.seed)
+        for layer in range(w.n_layers):
+            copies.append(dict(
+                q=torch.from_numpy(synthkv.queries(w, layer)).to(dev),
+                ck=torch.randint(0, w.n_centroids, (B, Hkv, t_cap * M), dtype=torch.uint8, device=dev, generator=g),
+                cv=torch.randint(0, w.n_centroids, (B, Hkv, t_cap * M), dtype=torch.uint8, device=dev, generator=g),
+                rk=torch.from_numpy(synthkv.recent_kv(w, layer, "k")).to(dev),
+                rv=torch.from_numpy(synthkv.recent_kv(w, layer, "v")).to(dev),
+                cbk=torch.from_numpy(synthkv.drawn_codebook(w, layer, "k")).to(dev),
+                cbv=torch.from_numpy(synthkv.drawn_codebook(w, layer, "v")).to(dev)))
+        npre = w.prefill_len
+        pre_cap = max(64, -(-npre // 64) * 64)
+        for tensor in ("k", "v"):
+            x = torch.from_numpy(synthkv.kv_values(w, 0, tensor, "prefill", npre)).to(dev)[None]
+            codes = torch.zeros((1, Hkv, pre_cap * M), dtype=torch.uint8, device=dev)
+            cb = copies[0]["cbk" if tensor == "k" else "cbv"]
+            P.encode(dims, x, cb, codes, pre_cap)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.encode_reps):
+                P.encode(dims, x, cb, codes, pre_cap)
+            e1.record()
+            torch.cuda.synchronize()
+            enc_ms[tensor] = e0.elapsed_time(e1) / args.encode_reps
+            del x, codes
+        enc_tokens = npre * 2
+        calls_per_step = w.n_layers
     print(f"[bench] inputs + encode ready in {time.time() - t0:.1f}s; encode K {enc_ms['k']:.3f} ms, "
           f"V {enc_ms['v']:.3f} ms", file=sys.stderr, flush=True)
 
-    q = torch.from_numpy(synthkv.queries(w)).to(dev)
-    rk = torch.from_numpy(synthkv.recent_kv(w, 0, "k")).to(dev)
-    rv = torch.from_numpy(synthkv.recent_kv(w, 0, "v")).to(dev)
-    hist_len = torch.tensor(w.hist_len, dtype=torch.int32, device=dev)
-    recent_len = torch.full((B,), R, dtype=torch.int32, device=dev)
-
-    # every input of a call is rotated, codebooks included, so no call finds its
-    # data in the caches the previous calls filled
-    copies = []
-    for i in range(args.copies):
-        copies.append(dict(q=q.clone(), ck=planes["k"].clone(), cv=planes["v"].clone(), rk=rk.clone(),
-                           rv=rv.clone(), cbk=cbk.clone(), cbv=cbv.clone()))
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     ws_bytes = P.decode_workspace_bytes(dims, B, T)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
-    def step(i):
-        c = copies[i % len(copies)]
+    def call(c):
         P.decode_attention(dims, c["q"], c["cbk"], c["cbv"], c["ck"], c["cv"], t_cap, hist_len, T, c["rk"],
                            c["rv"], recent_len, scale, out, lse, ws)
+
+    def step(i):
+        if calls_per_step == 1:
+            call(copies[i % len(copies)])
+        else:
+            for c in copies:
+                call(c)
 
     for i in range(args.warmup):
         step(i)
@@ -176,9 +224,9 @@ def main():
     kv_tokens = w.n_layers * (sum(w.hist_len) + B * R)
     value = kv_tokens / (ms * 1e-3)
     abytes = algorithmic_bytes(w, R)
-    achieved = abytes / (ms * 1e-3) / 1e9
+    call_ms = ms / calls_per_step
+    achieved = abytes / (call_ms * 1e-3) / 1e9
 
-    enc_tokens = B * T * 2  # K and V tensors of every history token
     enc_total_ms = enc_ms["k"] + enc_ms["v"]
     enc_tok_s = enc_tokens / (enc_total_ms * 1e-3)
     # brute-force encode work: per (token, head, subspace, centroid) d_sub subtractions and d_sub FMAs
@@ -200,15 +248,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "d_sub": w.d_sub, "centroids": w.n_centroids, "hist_tokens": T, "recent_tokens": R,
-                   "codes": "u8", "kv_dtype": w.dtype, "rotating_copies": args.copies},
+                   "layers": w.n_layers, "codes": "u8", "kv_dtype": w.dtype,
+                   "rotating_copies": args.copies if calls_per_step == 1 else w.n_layers},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "kernel": "pq_decode_kernel (one launch per pqkv_decode_attention call)",
-                     "algorithmic_bytes_per_call": abytes},
+                     "algorithmic_bytes_per_call": abytes, "us_per_call": round(call_ms * 1e3, 3)},
         "encode": {"tokens_per_s": round(enc_tok_s, 1), "ms": round(enc_total_ms, 4),
+                   "what": "K+V of the history" if calls_per_step == 1 else "K+V of one layer's prefill",
                    "tokens": enc_tokens, "bound": "alu", "achieved_tflops": round(enc_tflops, 2),
                    "peak_tflops": FP32_VALU_PEAK_TFLOPS, "frac": round(enc_tflops / FP32_VALU_PEAK_TFLOPS, 4),
-                   "hbm_gbs": round(encode_bytes(w, B * T) / (enc_total_ms * 1e-3) / 1e9, 1)},
+                   "hbm_gbs": round(encode_bytes(w, enc_tokens // 2) / (enc_total_ms * 1e-3) / 1e9, 1)},
     }
     for c in copies:
         c.clear()
