@@ -193,6 +193,23 @@ def main():
     print(f"[bench] inputs + encode ready in {time.time() - t0:.1f}s; encode K {enc_ms['k']:.3f} ms, "
           f"V {enc_ms['v']:.3f} ms", file=sys.stderr, flush=True)
 
+    # offline codebook training (pqkv_fit_codebooks) on one tensor's calibration draw
+    fit = None
+    if w.n_calib > 0:
+        cal = torch.from_numpy(synthkv.calibration_kv(w, 0, "k")).to(dev)
+        order = torch.from_numpy(synthkv.init_order(w, 0, "k", cal.shape[0]).astype(np.int32)).to(dev)
+        cb_fit = torch.empty((Hkv, w.n_centroids, M, w.d_sub), dtype=torch.float32, device=dev)
+        P.fit_codebooks(dims, cal, order, w.kmeans_iters, cb_fit)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        P.fit_codebooks(dims, cal, order, w.kmeans_iters, cb_fit)
+        e1.record()
+        torch.cuda.synchronize()
+        fit = {"ms_per_tensor": round(e0.elapsed_time(e1), 3), "points": int(cal.shape[0]),
+               "problems": Hkv * M, "centroids": w.n_centroids, "iters": w.kmeans_iters, "arith": "f64"}
+        del cal, order, cb_fit
+
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     ws_bytes = P.decode_workspace_bytes(dims, B, T)
@@ -260,6 +277,8 @@ def main():
                    "peak_tflops": FP32_VALU_PEAK_TFLOPS, "frac": round(enc_tflops / FP32_VALU_PEAK_TFLOPS, 4),
                    "hbm_gbs": round(encode_bytes(w, enc_tokens // 2) / (enc_total_ms * 1e-3) / 1e9, 1)},
     }
+    if fit is not None:
+        result["fit_codebooks"] = fit
     for c in copies:
         c.clear()
     torch.cuda.synchronize()

@@ -15,12 +15,13 @@ import torch  # loads the HIP runtime libpqkv.so binds to (same soname)
 
 __all__ = [
     "PQKVError", "Dims", "lib", "LIB_PATH", "encode", "build_lut", "decode_workspace_bytes",
-    "decode_attention", "append_kv", "merge", "code_plane_bytes", "F16", "F32", "MAX_RECENT", "TILE_TOKENS",
+    "decode_attention", "append_kv", "fit_codebooks", "merge", "code_plane_bytes", "MAX_FIT_POINTS", "F16", "F32", "MAX_RECENT", "TILE_TOKENS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpqkv.so")
 F16, F32 = 0, 1
 MAX_RECENT = 1024
+MAX_FIT_POINTS = 8192
 TILE_TOKENS = 64
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace missing or too small",
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.pqkv_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                      i64, i64, vp]
         L.pqkv_append_kv.restype = i32
+        L.pqkv_fit_codebooks.argtypes = [dp, vp, i32, i64, i64, i64, vp, i32, vp, vp, vp]
+        L.pqkv_fit_codebooks.restype = i32
         L.pqkv_merge.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp]
         L.pqkv_merge.restype = i32
         L.pqkv_status_str.argtypes = [i32]
@@ -196,6 +199,26 @@ def append_kv(dims: Dims, new_k, new_v, recent_k, recent_v, hist_len_in, recent_
         recent_k.shape[2], _ptr(hist_len_in), _ptr(recent_len_in), _ptr(hist_len_out), _ptr(recent_len_out),
         n_roll, _ptr(codebook_k), _ptr(codebook_v), _ptr(codes_k), _ptr(codes_v), t_cap, max_hist_len,
         _stream()))
+
+
+def fit_codebooks(dims: Dims, x, order, iters: int, codebook, kept=None) -> None:
+    """pqkv_fit_codebooks.  x: [N, Hkv, d] (rows contiguous); order: int32 [Hkv, M, N];
+    codebook: fp32 out [Hkv, K, M, d_sub]; kept: int32 out [Hkv, M] or None."""
+    _dev(x, order, codebook, kept)
+    if x.stride(2) != 1:
+        raise ValueError("x rows must be contiguous")
+    if order.dtype != torch.int32 or not order.is_contiguous():
+        raise ValueError("order must be contiguous int32")
+    if codebook.dtype != torch.float32 or not codebook.is_contiguous():
+        raise ValueError("codebook must be contiguous fp32")
+    if kept is not None and (kept.dtype != torch.int32 or not kept.is_contiguous()):
+        raise ValueError("kept must be contiguous int32")
+    n = x.shape[0]
+    if order.numel() < dims.n_kv_heads * dims.n_sub * n:
+        raise ValueError("order too small")
+    _check("pqkv_fit_codebooks", lib().pqkv_fit_codebooks(
+        ctypes.byref(dims), _ptr(x), _dtype_code(x), n, x.stride(0), x.stride(1), _ptr(order), iters,
+        _ptr(codebook), _ptr(kept), _stream()))
 
 
 def merge(out_a, lse_a, out_b, lse_b, out, lse) -> None:

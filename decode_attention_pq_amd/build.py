@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "pqkv")
 LIB = os.path.join(HERE, "libpqkv.so")
-SOURCES = ["encode.hip", "decode.hip", "aux_kernels.hip", "append.hip", "api.cpp"]
+SOURCES = ["encode.hip", "decode.hip", "aux_kernels.hip", "append.hip", "kmeans.hip", "api.cpp"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are switched off for all device code.

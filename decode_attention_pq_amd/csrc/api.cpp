@@ -237,4 +237,17 @@ pqkv_status pqkv_append_kv(const pqkv_dims* dims, int32_t batch, const void* new
                                     codebook_k, codebook_v, codes_k, codes_v, t_cap, stream));
 }
 
+pqkv_status pqkv_fit_codebooks(const pqkv_dims* dims, const void* x, pqkv_dtype x_dtype, int64_t n_points,
+                               int64_t x_tok_stride, int64_t x_head_stride, const int32_t* order,
+                               int32_t iters, float* codebook, int32_t* kept, hipStream_t stream) {
+    const pqkv_status ds = check_dims(dims);
+    if (ds != PQKV_OK) return ds;
+    if (!dtype_ok(x_dtype) || n_points < 1 || iters < 0 || x_tok_stride < 0 || x_head_stride < 0)
+        return PQKV_ERR_INVALID;
+    if (n_points > PQKV_MAX_FIT_POINTS || iters > 100000) return PQKV_ERR_UNSUPPORTED;
+    if (!x || !order || !codebook) return PQKV_ERR_INVALID;
+    return hip_status(launch_kmeans(*dims, x, x_dtype, n_points, x_tok_stride, x_head_stride, order, iters,
+                                    codebook, kept, stream));
+}
+
 }  // extern "C"

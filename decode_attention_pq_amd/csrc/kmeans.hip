@@ -1,0 +1,181 @@
+// pqkv_fit_codebooks: Lloyd k-means of every (kv head, subspace) codebook of one
+// tensor, on the GPU.
+//
+// MILLION write-up (DAC 2025), page "MILLION": the Fig. 5 paragraph clusters the
+// fused channels with k-means; the paragraph after it splits the head vector into
+// subspaces of dimension 2 or 4, one codebook per subspace; the Fig. 6 paragraph
+// trains the codebooks offline on calibration data.
+//
+// Per (head, subspace) problem, one work-group of 256 threads:
+//   1. the problem's n subvectors are staged in LDS (fp32 holds fp16/fp32 inputs
+//      exactly);
+//   2. initialisation: walk the given permutation and keep each point that is not
+//      equal to one already kept, until K are kept (one wave; every candidate is
+//      compared against the kept ones across the lanes, then a ballot); if fewer
+//      than K distinct points exist, the remaining slots copy slot 0;
+//   3. `iters` Lloyd iterations: every point takes its nearest centroid (squared
+//      distance, strict '<' in ascending centroid order, so the lowest index wins
+//      ties), then thread c moves centroid c to the mean of its members, summing
+//      them in point order; an empty cluster keeps its centroid.
+// Arithmetic is fp64 with every product and sum rounded on its own (no fused
+// multiply-add), so distances, sums and means are the IEEE results of the plain
+// definition, whatever the thread count.
+
+#include "pqkv_internal.h"
+
+#include <hip/hip_fp16.h>
+
+namespace pqkv {
+namespace {
+
+constexpr int kKmThreads = 256;
+
+template <typename XT>
+__device__ inline float elem(const XT* p) {
+    if constexpr (sizeof(XT) == 2)
+        return __half2float(*reinterpret_cast<const __half*>(p));
+    else
+        return *reinterpret_cast<const float*>(p);
+}
+
+template <int DSUB>
+__device__ inline double sqdist(const float* x, const double* c) {
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < DSUB; ++j) {
+        const double t = __dsub_rn((double)x[j], c[j]);
+        s = __dadd_rn(s, __dmul_rn(t, t));
+    }
+    return s;
+}
+
+struct KmArgs {
+    const void* x;
+    int64_t n, s_tok, s_head;
+    const int32_t* order;
+    int iters, K, M, Hkv;
+    float* cb;
+    int32_t* kept;
+};
+
+template <int DSUB, typename XT>
+__global__ __launch_bounds__(kKmThreads) void kmeans_kernel(KmArgs a) {
+    extern __shared__ float dyn[];
+    __shared__ double C[kLdsRows * DSUB];
+    __shared__ int kept_s;
+    const int m = blockIdx.x;
+    const int h = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int64_t n = a.n;
+    const int K = a.K;
+    float* pts = dyn;                                                   // [n][DSUB]
+    uint8_t* asg = reinterpret_cast<uint8_t*>(dyn + n * DSUB);          // [n]
+
+    const XT* x = static_cast<const XT*>(a.x) + h * a.s_head + m * DSUB;
+    for (int64_t i = tid; i < n; i += kKmThreads)
+#pragma unroll
+        for (int j = 0; j < DSUB; ++j) pts[i * DSUB + j] = elem(x + i * a.s_tok + j);
+    __syncthreads();
+
+    // ---- initialisation (wave 0)
+    if (tid < 64) {
+        const int32_t* ord = a.order + ((int64_t)h * a.M + m) * n;
+        int kept = 0;
+        for (int64_t i = 0; i < n && kept < K; ++i) {
+            const int32_t pi = ord[i];
+            if (pi < 0 || pi >= n) continue;  // not a point index
+            const float* p = pts + (int64_t)pi * DSUB;
+            bool dup = false;
+            for (int k = tid; k < kept; k += 64) {
+                bool same = true;
+#pragma unroll
+                for (int j = 0; j < DSUB; ++j) same = same && C[k * DSUB + j] == (double)p[j];
+                dup = dup || same;
+            }
+            if (!__any(dup)) {
+                if (tid == 0)
+#pragma unroll
+                    for (int j = 0; j < DSUB; ++j) C[kept * DSUB + j] = (double)p[j];
+                ++kept;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+        if (tid == 0) kept_s = kept;
+    }
+    __syncthreads();
+    const int kept = kept_s;
+    for (int k = kept + tid; k < K; k += kKmThreads)
+#pragma unroll
+        for (int j = 0; j < DSUB; ++j) C[k * DSUB + j] = kept > 0 ? C[j] : 0.0;
+    __syncthreads();
+
+    // ---- Lloyd iterations
+    for (int it = 0; it < a.iters; ++it) {
+        for (int64_t i = tid; i < n; i += kKmThreads) {
+            const float* p = pts + i * DSUB;
+            int best = 0;
+            double bd = sqdist<DSUB>(p, C);
+            for (int c = 1; c < K; ++c) {
+                const double dc = sqdist<DSUB>(p, C + c * DSUB);
+                if (dc < bd) {
+                    bd = dc;
+                    best = c;
+                }
+            }
+            asg[i] = (uint8_t)best;
+        }
+        __syncthreads();
+        // the update reads only assignments and points, so centroid c can be
+        // replaced as soon as its own sums are done
+        if (tid < K) {
+            double sum[DSUB];
+#pragma unroll
+            for (int j = 0; j < DSUB; ++j) sum[j] = 0.0;
+            int64_t cnt = 0;
+            for (int64_t i = 0; i < n; ++i) {
+                if (asg[i] == tid) {
+                    ++cnt;
+#pragma unroll
+                    for (int j = 0; j < DSUB; ++j) sum[j] = __dadd_rn(sum[j], (double)pts[i * DSUB + j]);
+                }
+            }
+            if (cnt > 0)
+#pragma unroll
+                for (int j = 0; j < DSUB; ++j) C[tid * DSUB + j] = __ddiv_rn(sum[j], (double)cnt);
+        }
+        __syncthreads();
+    }
+
+    if (tid < K)
+#pragma unroll
+        for (int j = 0; j < DSUB; ++j)
+            a.cb[(((int64_t)h * K + tid) * a.M + m) * DSUB + j] = __double2float_rn(C[tid * DSUB + j]);
+    if (a.kept && tid == 0) a.kept[(int64_t)h * a.M + m] = kept;
+}
+
+template <int DSUB, typename XT>
+hipError_t launch_typed(const KmArgs& a, hipStream_t stream) {
+    const size_t dyn = (size_t)a.n * DSUB * sizeof(float) + (size_t)a.n;
+    auto kern = kmeans_kernel<DSUB, XT>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.M, (unsigned)a.Hkv), dim3(kKmThreads), dyn, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t kmeans_lds_bytes(int d_sub, int64_t n) { return (size_t)n * d_sub * sizeof(float) + (size_t)n; }
+
+hipError_t launch_kmeans(const pqkv_dims& d, const void* x, pqkv_dtype xt, int64_t n, int64_t s_tok,
+                         int64_t s_head, const int32_t* order, int32_t iters, float* cb, int32_t* kept,
+                         hipStream_t stream) {
+    KmArgs a{x, n, s_tok, s_head, order, iters, d.n_centroids, d.head_dim / d.d_sub, d.n_kv_heads, cb, kept};
+    if (d.d_sub == 2)
+        return xt == PQKV_F16 ? launch_typed<2, __half>(a, stream) : launch_typed<2, float>(a, stream);
+    return xt == PQKV_F16 ? launch_typed<4, __half>(a, stream) : launch_typed<4, float>(a, stream);
+}
+
+}  // namespace pqkv

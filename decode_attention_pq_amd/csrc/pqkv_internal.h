@@ -76,6 +76,10 @@ hipError_t launch_append(const pqkv_dims& d, int32_t batch, const void* new_k, c
                          int32_t* recent_out, int32_t n_roll, const float* cb_k, const float* cb_v,
                          uint8_t* codes_k, uint8_t* codes_v, int64_t t_cap, hipStream_t stream);
 
+hipError_t launch_kmeans(const pqkv_dims& d, const void* x, pqkv_dtype xt, int64_t n, int64_t s_tok,
+                         int64_t s_head, const int32_t* order, int32_t iters, float* cb, int32_t* kept,
+                         hipStream_t stream);
+
 hipError_t launch_merge_states(int64_t n_rows, int32_t head_dim, const float* out_a,
                                const float* lse_a, const float* out_b, const float* lse_b,
                                float* out, float* lse, hipStream_t stream);

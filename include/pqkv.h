@@ -78,6 +78,9 @@ typedef struct {
 /* Largest recent window (r_cap) pqkv_decode_attention accepts. */
 #define PQKV_MAX_RECENT 1024
 
+/* Most calibration points per (kv head, subspace) pqkv_fit_codebooks takes. */
+#define PQKV_MAX_FIT_POINTS 8192
+
 /*
  * pqkv_encode -- nearest-centroid codes for a block of tokens (the online
  * prefill quantisation of the Fig. 6 paragraph; the subspace split of the
@@ -212,6 +215,40 @@ pqkv_status pqkv_append_kv(const pqkv_dims* dims, int32_t batch, const void* new
                            int32_t* recent_len_out, int32_t n_roll, const float* codebook_k,
                            const float* codebook_v, uint8_t* codes_k, uint8_t* codes_v, int64_t t_cap,
                            int64_t max_hist_len, hipStream_t stream);
+
+/*
+ * pqkv_fit_codebooks -- offline codebook training: Lloyd k-means of every
+ * (kv head, subspace) codebook of one tensor on calibration vectors (the Fig. 5
+ * paragraph clusters with k-means; the paragraph after it trains one codebook
+ * per subspace of dimension d_sub; the Fig. 6 paragraph does it offline).
+ *
+ * For every kv head h and subspace m, with the n_points subvectors
+ *     p_i = x[i][h][m*d_sub .. m*d_sub + d_sub - 1]:
+ *   1. initialisation: walk order[h][m][0..n_points-1] and keep each p_order[i] that is not
+ *      equal (all d_sub values) to one already kept, until K are kept; entries outside
+ *      [0, n_points) are skipped; if fewer than K distinct points exist, the remaining
+ *      centroids copy centroid 0;
+ *   2. `iters` Lloyd iterations: every point takes its nearest centroid by squared distance
+ *      (lowest index on exact ties), then every centroid with members moves to their mean;
+ *      an empty cluster keeps its centroid.
+ * All arithmetic is fp64 with every product, sum and quotient rounded on its own and member
+ * sums taken in point order, so the result is the exact IEEE evaluation of this definition
+ * (independent of the launch shape).  The fp64 centroids are rounded to fp32 at the end.
+ *
+ *   x            device, x_dtype (F16 or F32); element (i, h, e) at
+ *                x + i*x_tok_stride + h*x_head_stride + e (in elements), strides >= 0.
+ *   n_points     1..PQKV_MAX_FIT_POINTS.
+ *   order        device int32 [Hkv][M][n_points] (a permutation per problem: the random draw
+ *                of the initialisation, supplied by the caller).
+ *   iters        >= 0.
+ *   codebook     device fp32 out [Hkv][K][M][d_sub] (layout above), written whole.
+ *   kept         device int32 out [Hkv][M]: distinct points kept by the initialisation; may be NULL.
+ * Errors: INVALID for null pointers, n_points < 1, iters < 0, negative strides, bad dtype;
+ * UNSUPPORTED for dims outside the ranges above or n_points > PQKV_MAX_FIT_POINTS.
+ */
+pqkv_status pqkv_fit_codebooks(const pqkv_dims* dims, const void* x, pqkv_dtype x_dtype, int64_t n_points,
+                               int64_t x_tok_stride, int64_t x_head_stride, const int32_t* order,
+                               int32_t iters, float* codebook, int32_t* kept, hipStream_t stream);
 
 /*
  * pqkv_merge -- log-sum-exp merge of two normalised attention states over

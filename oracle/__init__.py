@@ -137,12 +137,13 @@ def lloyd(X, C0, iters: int):
     return C, assign, trace[: 2 * iters]
 
 
-def fit_codebooks(values, d_sub: int, K: int, iters: int, order) -> np.ndarray:
+def fit_codebooks(values, d_sub: int, K: int, iters: int, order, return_kept: bool = False):
     """Fit every (head, subspace) codebook of one tensor.
 
     values: [N, H, d] fp16/fp32 token-major; order: [H, M, N] permutations.
     Returns the fp32 codebook [H, K, M, d_sub] (the fp64 fit rounded to fp32,
-    which is the canonical codebook both sides consume)."""
+    which is the canonical codebook both sides consume), and with return_kept
+    also the distinct points the initialisation kept, [H, M]."""
     X = _f32(values)
     N, H, d = X.shape
     M = d // d_sub
@@ -153,7 +154,7 @@ def fit_codebooks(values, d_sub: int, K: int, iters: int, order) -> np.ndarray:
     rc = lib().orc_fit_codebooks(_ptr(X), N, H, d, d_sub, K, iters, _ptr(order), _ptr(cb), _ptr(kept))
     if rc != 0:
         raise ValueError("bad fit arguments")
-    return cb.astype(np.float32)
+    return (cb.astype(np.float32), kept) if return_kept else cb.astype(np.float32)
 
 
 # ---------------------------------------------------------------- O2 encode

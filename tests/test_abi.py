@@ -25,6 +25,7 @@ def _declared():
 def test_exports_every_declared_symbol(P):
     names = _declared()
     assert {"pqkv_encode", "pqkv_build_lut", "pqkv_decode_attention", "pqkv_merge", "pqkv_append_kv",
+            "pqkv_fit_codebooks",
             "pqkv_decode_workspace_bytes", "pqkv_status_str"} <= set(names)
     for n in names:
         assert hasattr(P.lib(), n), n
@@ -135,6 +136,18 @@ def test_append_validation(P):
     assert call(hout=F2) == 1 and call(rout=F3) == 1       # out lengths alias the in lengths
     assert call(hout=ctypes.c_void_p(0x20004)) == 1        # out overlaps in by one element
     assert call(rout=F4) == 1                              # the two out arrays overlap
+
+
+def test_fit_codebooks_validation(P):
+    L = P.lib()
+
+    def call(dims=(128, 2, 256, 32, 32), n=4096, iters=10, x=FAKE, order=FAKE, cb=FAKE, dt=0, ts=4096, hs=128):
+        return L.pqkv_fit_codebooks(_d(P, *dims), x, dt, n, ts, hs, order, iters, cb, None, None)
+
+    assert call(dims=(96, 2, 256, 32, 32)) == 2
+    assert call(n=0) == 1 and call(iters=-1) == 1 and call(ts=-1) == 1 and call(dt=9) == 1
+    assert call(n=8193) == 2                       # more points than one work-group stages
+    assert call(x=None) == 1 and call(order=None) == 1 and call(cb=None) == 1
 
 
 def test_product_path_does_not_touch_the_oracle():
