@@ -202,7 +202,8 @@ __device__ inline void load4(const __half* p, float (&v)[4]) {
 struct DecArgs {
     // first 64 bytes: everything the work mapping and the first loads need, so one
     // scalar load brings it in
-    int K, Hq, Hkv, n_groups, n_split, rounds, pstride, n_items;
+    int K, Hq, Hkv, n_groups, n_split, rounds, n_items;
+    int len_first;  // read the lengths before anything else (batches whose lengths may differ)
     int64_t split_tokens;
     const int32_t* hist_len;
     const int32_t* recent_len;
@@ -219,6 +220,7 @@ struct DecArgs {
     float scale_log2;
     float fix_scale;  // 2^S
     float fix_inv;    // 2^-S
+    int pstride;
     float* partials;
     uint32_t* counters;
     float* out;
@@ -257,15 +259,18 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     // XCD-aware work mapping: work-group ids that share an XCD (id mod 8) take
     // contiguous items, so all splits of one kv head meet in one L2.  The grid has
     // exactly n_items work-groups; XCD x holds ceil((n_items - x) / 8) of them.
+    // Items run head-major (all sequences of kv head 0, then of head 1, ...), so
+    // every XCD gets a share of every sequence even when their lengths differ.
     const int L = blockIdx.x;
     const int xcd = L & 7;
     const int item = xcd * (a.n_items >> 3) + (xcd < (a.n_items & 7) ? xcd : (a.n_items & 7)) + (L >> 3);
     const int unit = item / a.n_split;
     const int split = item - unit * a.n_split;
     const int grp = unit % a.n_groups;
-    const int bh = unit / a.n_groups;
-    const int h = bh % a.Hkv;
-    const int b = bh / a.Hkv;
+    const int hb = unit / a.n_groups;
+    const int batch = a.n_items / (a.Hkv * a.n_groups * a.n_split);
+    const int b = hb % batch;
+    const int h = hb / batch;
     const int hq0 = h * (a.Hq / a.Hkv) + grp * QH;
     const int K = a.K;
 
@@ -277,6 +282,24 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     const int T_in = a.hist_len[len_idx];
     const int R_in = a.recent_len ? a.recent_len[len_idx] : 0;
     const int64_t t0 = (int64_t)split * a.split_tokens;
+    // A sequence uses the splits that hold its history (at least one, which also
+    // takes the recent window or gives the empty result); work-groups of the other
+    // splits have nothing to do.  When lengths may differ, they learn it before
+    // issuing any load.
+    auto splits_used = [&](int64_t Tc) -> int {  // lengths are int32 and split_tokens <= 2^13
+        const uint32_t st = (uint32_t)a.split_tokens;
+        return Tc > 0 ? (int)(((uint32_t)Tc + st - 1u) / st) : 1;
+    };
+    auto clamp_hist = [&](int64_t Tr) -> int64_t { return Tr < 0 ? 0 : (Tr > a.max_hist ? a.max_hist : Tr); };
+    if (a.len_first) {
+        int T_early = T_in;
+        asm volatile("" : "+v"(T_early));
+        if (split >= splits_used(clamp_hist(T_early))) {
+            __builtin_amdgcn_s_waitcnt(0);
+            return;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // nothing below moves above the check
     const int64_t tile0 = t0 / kTileTokens;
     const int rounds = a.rounds;
 
@@ -320,12 +343,16 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     int T_v = T_in, R_v = R_in;
     asm volatile("" : "+v"(T_v), "+v"(R_v));  // first use of the lengths: here, not earlier
-    int64_t T = T_v;
-    T = T < 0 ? 0 : (T > a.max_hist ? a.max_hist : T);
+    const int64_t T = clamp_hist(T_v);
+    const int ns = splits_used(T);
+    if (split >= ns) {  // loads are in flight: let them land before the work-group ends
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
     const int64_t t1 = T < t0 + a.split_tokens ? T : t0 + a.split_tokens;
     int R = R_v;
     R = R < 0 ? 0 : (R > a.r_cap ? (int)a.r_cap : R);
-    const int rs_per = (R + a.n_split - 1) / a.n_split;
+    const int rs_per = (R + ns - 1) / ns;
     const int r0 = split * rs_per;
     const int n_rec = R - r0 < rs_per ? (R - r0 > 0 ? R - r0 : 0) : rs_per;
     const bool has_hist = t0 < t1;
@@ -681,7 +708,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     __syncthreads();
     if (tid == 0) {
         const uint32_t done = __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (done == (uint32_t)(a.n_split - 1));
+        last_flag = (done == (uint32_t)(ns - 1));
     }
     __syncthreads();
     if (!last_flag) return;
@@ -693,11 +720,11 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         const int el = e - j * D;
         const float* prow = prow0 + j * head_step;
         float mall = -INFINITY, l = 0.0f, o = 0.0f;
-        for (int s0 = 0; s0 < a.n_split; s0 += 8) {
+        for (int s0 = 0; s0 < ns; s0 += 8) {
             float pm[8], pl[8], po[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int sp = s0 + u < a.n_split ? s0 + u : a.n_split - 1;
+                const int sp = s0 + u < ns ? s0 + u : ns - 1;
                 const float* ps = prow + (int64_t)sp * a.pstride;
                 pm[u] = collect(ps + D);
                 pl[u] = collect(ps + D + 1);
@@ -706,7 +733,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
             float cm = -INFINITY;
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (s0 + u < a.n_split) cm = fmaxf(cm, pm[u]);
+                if (s0 + u < ns) cm = fmaxf(cm, pm[u]);
             if (cm == -INFINITY) continue;
             const float mnew = fmaxf(mall, cm);
             const float r = exp2f(mall - mnew);  // 0 while nothing has been folded in
@@ -714,7 +741,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
             o *= r;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                if (s0 + u < a.n_split && pm[u] != -INFINITY) {
+                if (s0 + u < ns && pm[u] != -INFINITY) {
                     const float wgt = exp2f(pm[u] - mnew);
                     l = fmaf(wgt, pl[u], l);
                     o = fmaf(wgt, po[u], o);
@@ -766,6 +793,7 @@ hipError_t launch_typed(const pqkv_dims& d, int32_t batch, const DecodePlan& pla
     k.Hkv = d.n_kv_heads;
     k.n_groups = plan.n_groups;
     k.n_split = plan.n_split;
+    k.len_first = batch > 1;
     k.rounds = plan.rounds;
     k.pstride = plan.partial_stride;
     k.split_tokens = plan.split_tokens;

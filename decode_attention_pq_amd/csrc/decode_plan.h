@@ -1,0 +1,65 @@
+// The decode path's constants, split plan and kernel arguments (host side).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/pqkv.h"
+
+namespace pqkv {
+
+constexpr int kTileTokens = 64;      // tokens per code tile (one per lane)
+constexpr int kDecodeThreads = 512;  // decode work-group: 8 wave64s
+constexpr int kDecodeWaves = kDecodeThreads / 64;
+constexpr int kTokensPerRound = kDecodeWaves * kTileTokens;  // one tile per wave per round
+constexpr int kPlanCUs = 256;         // MI355X compute units the split plan fills
+constexpr int kLdsRows = 256;         // LDS table rows (any uint8 code stays in bounds)
+
+// Tiles per wave in one decode split: each tile's scores stay in registers until
+// the split's softmax max is known, and the fully unrolled tile loop of the
+// kernel (rounds x M code bytes per lane) stays well inside the instruction cache.
+constexpr int decode_max_rounds(int n_sub, int qh) { return (n_sub == 64 || qh == 4) ? 8 : 16; }
+// Splits per unit the merge can take (its split maxima and sums live in LDS).
+constexpr int kMaxSplits = 512;
+
+// How a decode call is cut into work-groups.
+struct DecodePlan {
+    int qh;              // query heads per work-group (share one kv head)
+    int n_groups;        // query-head groups per kv head (= g / qh)
+    int rounds;          // tiles per wave (tokens per split = rounds * 512)
+    int n_split;         // splits over the history per (sequence, kv head, group)
+    int64_t split_tokens;
+    int partial_stride;  // floats per partial record: d outputs + max + sum, padded
+    int64_t units;       // (sequence, kv head, group) units, one completion counter each
+    size_t counters_offset;  // byte offset of the counters inside the workspace
+    size_t workspace_bytes;
+};
+
+DecodePlan plan_decode(const pqkv_dims& d, int32_t batch, int64_t max_hist_len);
+
+struct DecodeArgs {
+    const void* q;
+    const float* cb_k;
+    const float* cb_v;
+    const uint8_t* codes_k;
+    const uint8_t* codes_v;
+    int64_t t_cap;
+    const int32_t* hist_len;
+    int64_t max_hist;
+    const void* rk;
+    const void* rv;
+    int64_t r_cap;
+    const int32_t* recent_len;
+    float scale_log2;  // softmax scale * log2(e)
+    float* out;
+    float* lse;
+    float* partials;
+    uint32_t* counters;
+};
+
+hipError_t launch_decode(const pqkv_dims& d, int32_t batch, pqkv_dtype qt, pqkv_dtype rt,
+                         const DecodePlan& plan, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace pqkv
