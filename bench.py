@@ -29,6 +29,10 @@ METRIC = "PQ decode-attn KV tokens/s & % HBM peak at 32K ctx; pq_encode tokens/s
 HBM_PEAK_GBS = 8000.0
 # fp32 vector peak of MI355X: 256 CUs x 2.4 GHz x 128 lanes x 2 flops (packed FMA)
 FP32_VALU_PEAK_TFLOPS = 157.3
+# Unpacked 32-bit VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-operations/s
+# (the 157.3 TFLOP/s fp32 figure counts packed fp32 FMAs, two flops on two lanes per slot;
+# this code is built without packed fp32 instructions).
+VALU_LANE_OPS_PEAK_T = 256 * 4 * 16 * 2.4e9 / 1e12
 
 
 def parse():
@@ -247,8 +251,14 @@ def main():
     enc_total_ms = enc_ms["k"] + enc_ms["v"]
     enc_tok_s = enc_tokens / (enc_total_ms * 1e-3)
     # brute-force encode work: per (token, head, subspace, centroid) d_sub subtractions and d_sub FMAs
-    enc_flops = enc_tokens * Hkv * M * w.n_centroids * (2 * w.d_sub)
+    enc_pairs = enc_tokens * Hkv * M * w.n_centroids  # (subvector, centroid) distance evaluations
+    enc_flops = enc_pairs * (2 * w.d_sub)
     enc_tflops = enc_flops / (enc_total_ms * 1e-3) / 1e12
+    # VALU instructions per pair in the compiled scan loop: d_sub subtractions, one multiply,
+    # d_sub - 1 fused multiply-adds, a compare, two selects, and one index move per pair plus
+    # one per four pairs of loop bookkeeping (gfx950 asm of encode_kernel)
+    enc_ops_per_pair = 2 * w.d_sub + 4.25
+    enc_tops = enc_pairs * enc_ops_per_pair / (enc_total_ms * 1e-3) / 1e12
 
     result = {
         "metric": METRIC,
@@ -273,8 +283,10 @@ def main():
                      "algorithmic_bytes_per_call": abytes, "us_per_call": round(call_ms * 1e3, 3)},
         "encode": {"tokens_per_s": round(enc_tok_s, 1), "ms": round(enc_total_ms, 4),
                    "what": "K+V of the history" if calls_per_step == 1 else "K+V of one layer's prefill",
-                   "tokens": enc_tokens, "bound": "alu", "achieved_tflops": round(enc_tflops, 2),
-                   "peak_tflops": FP32_VALU_PEAK_TFLOPS, "frac": round(enc_tflops / FP32_VALU_PEAK_TFLOPS, 4),
+                   "tokens": enc_tokens, "bound": "alu", "valu_ops_per_pair": enc_ops_per_pair,
+                   "achieved": round(enc_tops, 2), "peak": round(VALU_LANE_OPS_PEAK_T, 2), "unit": "T VALU lane-ops/s",
+                   "frac": round(enc_tops / VALU_LANE_OPS_PEAK_T, 4),
+                   "flop_form_tflops": round(enc_tflops, 2), "fp32_peak_tflops": FP32_VALU_PEAK_TFLOPS,
                    "hbm_gbs": round(encode_bytes(w, enc_tokens // 2) / (enc_total_ms * 1e-3) / 1e9, 1)},
     }
     if fit is not None:
