@@ -386,6 +386,12 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int s = 0; s < P; ++s) issue(ring[s], s);
 
+    // zero the histogram now, while the codebook is on its way (phase 1 reads only the
+    // LUT region; the barrier before phase 1 orders these stores before any atomic)
+    if (has_hist)
+        for (int e = tid; e < K * kRow / 4; e += kThreads)
+            reinterpret_cast<uint4*>(hist)[e] = make_uint4(0u, 0u, 0u, 0u);
+
     // ---- 2. ad-LUT in LDS, recent-window scores, per-lane subspace offsets
 #pragma unroll
     for (int j = 0; j < QH; ++j) {
@@ -482,11 +488,6 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
                 sc[s][j] = tok_ok ? (acc[j][0] + acc[j][1]) + (acc[j][2] + acc[j][3]) : -INFINITY;
         }
     }
-
-    // zero the histogram (its region is not touched before phase 2)
-    if (has_hist)
-        for (int e = tid; e < K * kRow / 4; e += kThreads)
-            reinterpret_cast<uint4*>(hist)[e] = make_uint4(0u, 0u, 0u, 0u);
 
     // ---- 4. work-group max over history and recent scores
 #pragma unroll
