@@ -242,6 +242,61 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     assert torch.isfinite(out).all() and torch.isfinite(lse).all(), "non-finite decode output"
 
+    # per-call distribution: a second pass with an event pair around every call
+    # (the headline above is the batch mean, which has no per-call event overhead)
+    nper = min(args.steps, 100)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nper)]
+    for i in range(nper):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    per_call_us = sorted(a.elapsed_time(b) * 1e3 / calls_per_step for a, b in evs)
+    pct = lambda p: round(per_call_us[min(len(per_call_us) - 1, int(p * len(per_call_us)))], 3)
+
+    # the live-cache step: one new row per sequence, with and without a roll into the history
+    append_us = None
+    if calls_per_step == 1 and R > 1:
+        c0 = copies[0]
+        r_cap = R
+        n_roll = R // 2
+        nk = torch.zeros((B, Hkv, d), dtype=c0["rk"].dtype, device=dev)
+        lens = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)]  # hist, recent (in / out pairs)
+        rk_a, rv_a = c0["rk"].clone(), c0["rv"].clone()
+        ck_a, cv_a = c0["ck"].clone(), c0["cv"].clone()
+
+        def append(src, dst):
+            P.append_kv(dims, nk, nk, rk_a, rv_a, lens[src], lens[src + 1], lens[dst], lens[dst + 1], n_roll,
+                        c0["cbk"], c0["cbv"], ck_a, cv_a, t_cap, T - n_roll)
+
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # 20 steps back to back, none of them rolls
+        lens[0].fill_(T - n_roll)
+        lens[1].fill_(r_cap - 21)
+        torch.cuda.synchronize()
+        a0.record()
+        for i in range(20):
+            append(2 * (i % 2), 2 * ((i + 1) % 2))
+        a1.record()
+        torch.cuda.synchronize()
+        no_roll = round(a0.elapsed_time(a1) * 1e3 / 20, 2)
+        # single steps that roll (median of 10)
+        res = []
+        for _ in range(10):
+            lens[0].fill_(T - n_roll)
+            lens[1].fill_(r_cap)
+            torch.cuda.synchronize()
+            a0.record()
+            append(0, 2)
+            a1.record()
+            torch.cuda.synchronize()
+            res.append(a0.elapsed_time(a1) * 1e3)
+        roll = round(sorted(res)[len(res) // 2], 2)
+        # the no-roll step is two tiny launches; back to back from Python it measures the host
+        # launch path, not the GPU
+        append_us = {"no_roll_host_bound": no_roll, "roll_single": roll, "n_roll": n_roll, "r_cap": r_cap}
+        del rk_a, rv_a, ck_a, cv_a
+
     kv_tokens = w.n_layers * (sum(w.hist_len) + B * R)
     value = kv_tokens / (ms * 1e-3)
     abytes = algorithmic_bytes(w, R)
@@ -280,7 +335,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "kernel": "pq_decode_kernel (one launch per pqkv_decode_attention call)",
-                     "algorithmic_bytes_per_call": abytes, "us_per_call": round(call_ms * 1e3, 3)},
+                     "algorithmic_bytes_per_call": abytes, "us_per_call": round(call_ms * 1e3, 3),
+                     "per_call_us": {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9)}},
         "encode": {"tokens_per_s": round(enc_tok_s, 1), "ms": round(enc_total_ms, 4),
                    "what": "K+V of the history" if calls_per_step == 1 else "K+V of one layer's prefill",
                    "tokens": enc_tokens, "bound": "alu", "valu_ops_per_pair": enc_ops_per_pair,
@@ -291,6 +347,8 @@ def main():
     }
     if fit is not None:
         result["fit_codebooks"] = fit
+    if append_us is not None:
+        result["append_kv_us"] = append_us
     for c in copies:
         c.clear()
     torch.cuda.synchronize()

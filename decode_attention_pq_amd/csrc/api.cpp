@@ -215,7 +215,7 @@ pqkv_status pqkv_append_kv(const pqkv_dims* dims, int32_t batch, const void* new
     if (!dtype_ok(recent_dtype)) return PQKV_ERR_INVALID;
     if (batch < 0 || r_cap < 1 || n_roll < 1 || n_roll > r_cap || max_hist_len < 0) return PQKV_ERR_INVALID;
     if (t_cap <= 0 || t_cap % kTileTokens || max_hist_len + n_roll > t_cap) return PQKV_ERR_INVALID;
-    if (r_cap > PQKV_MAX_RECENT || n_roll > 512 || batch > 65535) return PQKV_ERR_UNSUPPORTED;
+    if (r_cap > PQKV_MAX_RECENT || n_roll > 512 || batch > 32767) return PQKV_ERR_UNSUPPORTED;
     if (batch == 0) return PQKV_OK;
     if (!new_k || !new_v || !recent_k || !recent_v || !hist_len_in || !recent_len_in || !hist_len_out ||
         !recent_len_out || !codebook_k || !codebook_v || !codes_k || !codes_v)

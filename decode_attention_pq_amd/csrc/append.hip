@@ -7,14 +7,18 @@
 // path.  Rolling n_roll tokens at once is that batched, delayed quantisation; the
 // codes are the nearest-centroid codes of pqkv_encode.
 //
-// Work decomposition: one work-group per (kv head, sequence, tensor K or V).
-// Every work-group reads the old lengths; the (h = 0, K) work-group of a sequence
-// writes the new ones to separate arrays, so no work-group can see a length that
-// another has already advanced.  A rolling work-group stages its head's codebook
-// in LDS, encodes one rolled token per thread, then moves the remaining rows down
-// in chunks of at most n_roll rows with a barrier after each chunk (a chunk
-// writes only rows that earlier chunks have finished reading), then writes the
-// new row.
+// Work decomposition: two kernels on the caller's stream.
+//   roll_kernel    one work-group of 8 waves per (64 rolled rows, kv head, sequence and
+//                  tensor): work-groups of sequences whose window is not full return at
+//                  once; the others stage the head's codebook in LDS and encode, wave w
+//                  taking subspaces [w*M/8, (w+1)*M/8) of the 64 rows (one row per lane).
+//   append_kernel  one work-group per (kv head, sequence, tensor): after the encode
+//                  has read them (stream order), the remaining rows of a full window
+//                  move down in chunks of at most n_roll rows with a barrier after each
+//                  chunk (a chunk writes only rows that earlier chunks have finished
+//                  reading), then the new row is written.  The (h = 0, K) work-group of a
+//                  sequence writes its new lengths to separate arrays, so no work-group
+//                  can see a length that another has already advanced.
 
 #include "nearest.h"
 
@@ -22,6 +26,11 @@ namespace pqkv {
 namespace {
 
 constexpr int kAppThreads = 512;
+constexpr int kAppWaves = kAppThreads / 64;
+constexpr int kRollSubspaces = 16;  // subspaces one roll work-group encodes (2 per wave)
+
+__device__ inline float to_float(float v) { return v; }
+__device__ inline float to_float(__half v) { return __half2float(v); }
 
 struct AppendArgs {
     const void* new_k;
@@ -42,46 +51,73 @@ struct AppendArgs {
     int K, Hkv;
 };
 
-template <int D, int DSUB, typename RT>
-__global__ __launch_bounds__(kAppThreads) void append_kernel(AppendArgs a) {
-    constexpr int M = D / DSUB;
-    constexpr int U = D * (int)sizeof(RT) / 16;  // 16-byte units per row
-    __shared__ float4 cbs4[kLdsRows * D / 4];
-    const float* cbs = reinterpret_cast<const float*>(cbs4);
+// The window of sequence b rolls in this call, and where its history goes.
+__device__ inline bool roll_ok(const AppendArgs& a, int64_t T, int64_t R, bool& rolls) {
+    const bool ok = T >= 0 && R >= 0 && R <= a.r_cap && (R < a.r_cap || T + a.n_roll <= a.t_cap);
+    rolls = ok && R == a.r_cap;
+    return ok;
+}
 
+template <int D, int DSUB, typename RT>
+__global__ __launch_bounds__(kAppThreads) void roll_kernel(AppendArgs a) {
+    constexpr int M = D / DSUB;
+    constexpr int SW = kRollSubspaces;       // subspaces per work-group
+    constexpr int MW = SW / kAppWaves;       // subspaces per wave
+    constexpr int CS = SW * DSUB;            // floats per staged centroid row
+    static_assert(M % SW == 0 && SW % kAppWaves == 0, "roll subspace split");
+    __shared__ float cbs[kLdsRows * CS];
+    const int g = blockIdx.x % (M / SW);     // subspace group
+    const int rb = blockIdx.x / (M / SW);    // block of 64 rolled rows
+    const int h = blockIdx.y;
+    const int b = blockIdx.z >> 1;
+    const int tensor = blockIdx.z & 1;       // 0 = K, 1 = V
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int64_t T = a.hist_in[b];
+    const int64_t R = a.recent_in[b];
+    bool rolls;
+    if (!roll_ok(a, T, R, rolls) || !rolls) return;
+
+    // stage subspaces [g*SW, g*SW + SW) of every centroid: CS contiguous floats per row
+    const float* cb = (tensor ? a.cb_v : a.cb_k) + (int64_t)h * a.K * D + g * CS;
+    for (int i = tid; i < a.K * CS; i += kAppThreads) cbs[i] = cb[(i / CS) * D + i % CS];
+    __syncthreads();
+    const int row = rb * 64 + lane;
+    if (row < a.n_roll) {
+        const RT* rows = static_cast<const RT*>(tensor ? a.rv : a.rk) + ((int64_t)b * a.Hkv + h) * a.r_cap * D;
+        const int m0 = g * SW + wave * MW;
+        float xv[MW * DSUB];
+#pragma unroll
+        for (int j = 0; j < MW * DSUB; ++j) xv[j] = to_float(rows[(int64_t)row * D + m0 * DSUB + j]);
+        uint8_t* plane = (tensor ? a.codes_v : a.codes_k) + ((int64_t)b * a.Hkv + h) * a.t_cap * M;
+        const int64_t t = T + row;
+        write_nearest_codes_slice<D, DSUB, MW, CS>(xv, cbs + wave * MW * DSUB, a.K, code_slot<M>(plane, t),
+                                                   (int)(t & (kTileTokens - 1)), m0);
+    }
+}
+
+template <int D, typename RT>
+__global__ __launch_bounds__(kAppThreads) void append_kernel(AppendArgs a) {
+    constexpr int U = D * (int)sizeof(RT) / 16;  // 16-byte units per row
     const int h = blockIdx.x;
     const int b = blockIdx.y;
     const int tensor = blockIdx.z;  // 0 = K, 1 = V
     const int tid = threadIdx.x;
-
     int64_t T = a.hist_in[b];
     int64_t R = a.recent_in[b];
     const int n_roll = a.n_roll;
-    const bool ok = T >= 0 && R >= 0 && R <= a.r_cap && (R < a.r_cap || T + n_roll <= a.t_cap);
-    if (!ok) {
+    bool rolls;
+    if (!roll_ok(a, T, R, rolls)) {
         if (h == 0 && tensor == 0 && tid == 0) {
             a.hist_out[b] = (int32_t)T;
             a.recent_out[b] = (int32_t)R;
         }
         return;
     }
-
     RT* rows = static_cast<RT*>(tensor ? a.rv : a.rk) + ((int64_t)b * a.Hkv + h) * a.r_cap * D;
-    if (R == a.r_cap) {
-        // roll: encode rows 0..n_roll-1 into history positions T..T+n_roll-1
-        const float* cb = (tensor ? a.cb_v : a.cb_k) + (int64_t)h * a.K * D;
-        const float4* src = reinterpret_cast<const float4*>(cb);
-        for (int i = tid; i < a.K * D / 4; i += kAppThreads) cbs4[i] = src[i];
-        __syncthreads();
-        uint8_t* plane = (tensor ? a.codes_v : a.codes_k) + ((int64_t)b * a.Hkv + h) * a.t_cap * M;
-        if (tid < n_roll) {
-            float xv[D];
-            Row<RT>::template load<D>(rows + (int64_t)tid * D, xv);
-            const int64_t t = T + tid;
-            write_nearest_codes<D, DSUB>(xv, cbs, a.K, code_slot<M>(plane, t), (int)(t & (kTileTokens - 1)));
-        }
-        __syncthreads();  // every rolled row has been read
-        // move rows n_roll..R-1 down to 0..R-n_roll-1
+    if (rolls) {
+        // move rows n_roll..R-1 down to 0..R-n_roll-1 (the roll kernel, earlier on the
+        // stream, has read rows 0..n_roll-1)
         uint4* r4 = reinterpret_cast<uint4*>(rows);
         const int64_t left = R - n_roll;
         const int chunk = n_roll < kAppThreads / U ? n_roll : kAppThreads / U;
@@ -108,8 +144,13 @@ __global__ __launch_bounds__(kAppThreads) void append_kernel(AppendArgs a) {
 
 template <int D, int DSUB, typename RT>
 hipError_t launch_typed(int32_t batch, const AppendArgs& a, hipStream_t stream) {
+    dim3 rgrid((unsigned)((a.n_roll + 63) / 64 * (D / DSUB / kRollSubspaces)), (unsigned)a.Hkv,
+               (unsigned)batch * 2u);
+    hipLaunchKernelGGL((roll_kernel<D, DSUB, RT>), rgrid, dim3(kAppThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     dim3 grid((unsigned)a.Hkv, (unsigned)batch, 2u);
-    hipLaunchKernelGGL((append_kernel<D, DSUB, RT>), grid, dim3(kAppThreads), 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<D, RT>), grid, dim3(kAppThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -86,6 +86,37 @@ __device__ inline void write_nearest_codes(const float (&xv)[D], const float* cb
     }
 }
 
+// The same for subspaces m0 .. m0 + MW - 1 only.  xv holds those subspaces' values
+// (MW * DSUB floats, subspace m0 first); `cbs` points at subspace m0 of centroid 0
+// of an on-chip codebook whose centroid rows are CS floats apart.
+template <int D, int DSUB, int MW, int CS>
+__device__ inline void write_nearest_codes_slice(const float (&xv)[MW * DSUB], const float* cbs, int K,
+                                                 uint8_t* dst, int slot, int m0) {
+    constexpr int M = D / DSUB;
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi) {
+        float best = INFINITY;
+        int bi = 0;
+        const float* cm = cbs + mi * DSUB;
+#pragma unroll 4
+        for (int c = 0; c < K; ++c) {
+            const float* cc = cm + c * CS;
+            float dd = 0.0f;
+#pragma unroll
+            for (int j = 0; j < DSUB; ++j) {
+                const float e = xv[mi * DSUB + j] - cc[j];
+                dd = fmaf(e, e, dd);
+            }
+            if (dd < best) {
+                best = dd;
+                bi = c;
+            }
+        }
+        const int p = (m0 + mi - slot) & (M - 1);
+        dst[(p >> 4) * (kTileTokens * 16) + (p & 15)] = (uint8_t)bi;
+    }
+}
+
 // Byte address of token t's slot-0 chunk in plane `plane` (t_cap*M bytes).
 template <int M>
 __device__ inline uint8_t* code_slot(uint8_t* plane, int64_t t) {

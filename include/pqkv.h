@@ -207,7 +207,7 @@ pqkv_status pqkv_decode_attention(const pqkv_dims* dims, int32_t batch, const vo
  * A sequence whose device lengths break these bounds is left unchanged and its
  * out lengths repeat the in lengths.  Errors: INVALID for null pointers, bad
  * sizes or alignment, overlapping length arrays, bad dtype; UNSUPPORTED for dims
- * outside the ranges above, r_cap > PQKV_MAX_RECENT, n_roll > 512 or batch > 65535.
+ * outside the ranges above, r_cap > PQKV_MAX_RECENT, n_roll > 512 or batch > 32767.
  */
 pqkv_status pqkv_append_kv(const pqkv_dims* dims, int32_t batch, const void* new_k, const void* new_v,
                            void* recent_k, void* recent_v, pqkv_dtype recent_dtype, int64_t r_cap,
