@@ -108,6 +108,12 @@ DECODE_CASES = [
     (64, 4, 64, 8, 2, (1500, 3), (2, 2), 4, np.float32),          # M=16: four query heads per work-group
     (128, 2, 256, 2, 2, (2000, 40), (0, 0), 0, np.float16),       # no recent window at all
     (128, 2, 256, 1, 1, (0,), (0,), 4, np.float16),               # nothing cached
+    # ragged batches: sequences that use fewer splits than the longest (their other
+    # work-groups exit early; the recent window goes to the splits in use), a window
+    # larger than one split's share, and units that straddle XCDs
+    (128, 2, 256, 2, 2, (100, 9000), (200, 3), 256, np.float16),
+    (128, 2, 256, 3, 3, (4096, 0, 17, 12000, 4097, 8191), (1, 64, 0, 5, 64, 2), 64, np.float16),
+    (128, 4, 256, 8, 2, (20000, 300, 0), (33, 0, 9), 64, np.float16),
 ]
 
 
