@@ -1,0 +1,59 @@
+"""Seeded sweep of random decode shapes against the oracle.
+
+Twenty-four shapes drawn from one seed cover the combinations the hand-written
+cases do not list: head size, subspace size, centroid count (2..256), kv and
+query heads (groups of 1, 2, 4 and 8), batch 1..5 with independent history
+lengths (empty, sub-tile, multi-split), recent windows from none to 300 rows,
+fp16 and fp32.  Every case runs the HIP decode through the C ABI and compares
+it with the dequantise-then-exact oracle at the usual tolerance.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synthkv
+from pqkv_testlib import check_attention, dims_for, run_gpu_decode, softmax_scale
+
+pytestmark = pytest.mark.gpu
+
+
+def _shapes(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([64, 128]))
+        dsub = int(rng.choice([2, 4]))
+        K = int(rng.choice([2, 7, 16, 64, 100, 255, 256]))
+        Hkv = int(rng.integers(1, 5))
+        g = int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.integers(1, 6))
+        kind = rng.integers(0, 4, size=B)
+        hist = tuple(int(v) for v in np.where(kind == 0, 0, np.where(kind == 1, rng.integers(1, 64, B),
+                                                                      rng.integers(64, 6000, B))))
+        r_cap = int(rng.choice([0, 1, 8, 64, 300]))
+        rec = tuple(int(v) for v in rng.integers(0, r_cap + 1, B)) if r_cap else (0,) * B
+        dt = np.float16 if rng.random() < 0.7 else np.float32
+        out.append((d, dsub, K, Hkv * g, Hkv, hist, rec, r_cap, dt))
+    return out
+
+
+@pytest.mark.parametrize("case", _shapes(), ids=lambda c: f"d{c[0]}s{c[1]}K{c[2]}h{c[3]}/{c[4]}b{len(c[5])}r{c[7]}")
+def test_random_shape_decode(case):
+    d, dsub, K, Hq, Hkv, hist, rec, r_cap, dt = case
+    B, M = len(hist), d // dsub
+    t_cap = max(64, -(-max(hist) // 64) * 64)
+    seed = 7000 + sum(hist) + K + d + Hq
+    q = synthkv.small_normal(seed, (B, Hq, d), dt)
+    cbk = (synthkv.small_normal(seed + 1, (Hkv, K, M, dsub)) * 1.5).astype(np.float32)
+    cbv = (synthkv.small_normal(seed + 2, (Hkv, K, M, dsub)) * 1.5).astype(np.float32)
+    ck = synthkv.small_codes(seed + 3, (B, Hkv, t_cap, M), K)
+    cv = synthkv.small_codes(seed + 4, (B, Hkv, t_cap, M), K)
+    rk = synthkv.small_normal(seed + 5, (B, Hkv, max(r_cap, 1), d), dt)[:, :, :r_cap]
+    rv = synthkv.small_normal(seed + 6, (B, Hkv, max(r_cap, 1), d), dt)[:, :, :r_cap]
+    scale = softmax_scale(d)
+    ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, hist, rk, rv, rec, scale)
+    dims = dims_for(d, dsub, K, Hq, Hkv)
+    out, lse = run_gpu_decode(dims, q, cbk, cbv, oracle.tile_codes(ck, t_cap), oracle.tile_codes(cv, t_cap), t_cap,
+                              hist, np.ascontiguousarray(rk) if r_cap else None,
+                              np.ascontiguousarray(rv) if r_cap else None, rec, scale)
+    check_attention(out, lse, ref_out, ref_lse)
