@@ -1,0 +1,43 @@
+/* A plain C program against libpqkv: it includes only include/pqkv.h, links the
+ * shared library and exercises the host-side contract (status strings, workspace
+ * sizes, argument validation) without touching a GPU. */
+#include <stdio.h>
+#include <string.h>
+
+#include "pqkv.h"
+
+static int fails = 0;
+#define EXPECT(cond)                                           \
+    do {                                                       \
+        if (!(cond)) {                                         \
+            printf("FAIL line %d: %s\n", __LINE__, #cond);     \
+            ++fails;                                           \
+        }                                                      \
+    } while (0)
+
+int main(void) {
+    pqkv_dims d = {128, 2, 256, 32, 32};
+    pqkv_dims bad = {96, 2, 256, 32, 32};
+    void* fake = (void*)0x10000; /* never dereferenced: validation fails first */
+
+    EXPECT(strcmp(pqkv_status_str(PQKV_OK), "ok") == 0);
+    EXPECT(pqkv_decode_workspace_bytes(&d, 1, 32768) == (size_t)(32 * 8 * 132 * 4 + 256));
+    EXPECT(pqkv_decode_workspace_bytes(&bad, 1, 32768) == 0);
+    EXPECT(pqkv_encode(&bad, fake, PQKV_F16, 1, 10, 0, 4096, 128, fake, fake, 64, 0, NULL) == PQKV_ERR_UNSUPPORTED);
+    EXPECT(pqkv_encode(&d, NULL, PQKV_F16, 1, 10, 0, 4096, 128, fake, fake, 64, 0, NULL) == PQKV_ERR_INVALID);
+    EXPECT(pqkv_encode(&d, NULL, PQKV_F16, 1, 0, 0, 4096, 128, NULL, NULL, 64, 0, NULL) == PQKV_OK);
+    EXPECT(pqkv_merge(0, 128, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == PQKV_OK);
+    EXPECT(pqkv_merge(4, 2048, fake, fake, fake, fake, fake, fake, NULL) == PQKV_ERR_UNSUPPORTED);
+    EXPECT(pqkv_fit_codebooks(&d, fake, PQKV_F16, 0, 4096, 128, fake, 10, fake, NULL, NULL) == PQKV_ERR_INVALID);
+    EXPECT(pqkv_append_kv(&d, 0, NULL, NULL, NULL, NULL, PQKV_F16, 128, NULL, NULL, NULL, NULL, 64, NULL, NULL,
+                          NULL, NULL, 4096, 100, NULL) == PQKV_OK);
+    {
+        int32_t lens[4];
+        EXPECT(pqkv_append_kv(&d, 1, fake, fake, fake, fake, PQKV_F16, 128, lens, lens + 1, lens, lens + 3, 64, fake,
+                              fake, fake, fake, 4096, 100, NULL) == PQKV_ERR_INVALID); /* out aliases in */
+    }
+    EXPECT(pqkv_decode_attention(&d, 1, fake, PQKV_F16, fake, fake, fake, fake, 32768, fake, 32768, fake, fake,
+                                 PQKV_F16, 128, fake, 0.088f, fake, fake, NULL, 0, NULL) == PQKV_ERR_WORKSPACE);
+    printf(fails ? "abi_check: %d failures\n" : "abi_check: ok\n", fails);
+    return fails != 0;
+}

@@ -150,6 +150,25 @@ def test_fit_codebooks_validation(P):
     assert call(x=None) == 1 and call(order=None) == 1 and call(cb=None) == 1
 
 
+def test_plain_c_program_against_the_abi(P, tmp_path):
+    """tests/abi_check.c includes only include/pqkv.h, links libpqkv.so with gcc as
+    C11 and checks the host-side contract without a GPU."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    libdir = os.path.dirname(P.LIB_PATH)
+    exe = str(tmp_path / "abi_check")
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", os.path.join(ROOT, "tests", "abi_check.c"), "-L", libdir, "-lpqkv",
+                    f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi_check: ok" in r.stdout
+
+
 def test_product_path_does_not_touch_the_oracle():
     pkg = os.path.join(ROOT, "decode_attention_pq_amd")
     for dirpath, _, files in os.walk(pkg):
