@@ -27,12 +27,12 @@ import numpy as np
 
 METRIC = "PQ decode-attn KV tokens/s & % HBM peak at 32K ctx; pq_encode tokens/s"
 HBM_PEAK_GBS = 8000.0
-# fp32 vector peak of MI355X: 256 CUs x 2.4 GHz x 128 lanes x 2 flops (packed FMA)
+# fp32 vector peak of MI355X (published): 157.3 TFLOP/s = 256 CUs x 2.4 GHz x 256 flops per
+# clock per CU, an FMA counting two flops.
 FP32_VALU_PEAK_TFLOPS = 157.3
-# Unpacked 32-bit VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-operations/s
-# (the 157.3 TFLOP/s fp32 figure counts packed fp32 FMAs, two flops on two lanes per slot;
-# this code is built without packed fp32 instructions).
-VALU_LANE_OPS_PEAK_T = 256 * 4 * 16 * 2.4e9 / 1e12
+# The same peak in VALU lane-operations (one 32-bit VALU instruction on one lane, an FMA
+# counted once): 78.65 T/s.  The encode scan is counted in these units.
+VALU_LANE_OPS_PEAK_T = FP32_VALU_PEAK_TFLOPS / 2
 
 
 def parse():
@@ -309,10 +309,11 @@ def main():
     enc_pairs = enc_tokens * Hkv * M * w.n_centroids  # (subvector, centroid) distance evaluations
     enc_flops = enc_pairs * (2 * w.d_sub)
     enc_tflops = enc_flops / (enc_total_ms * 1e-3) / 1e12
-    # VALU instructions per pair in the compiled scan loop: d_sub subtractions, one multiply,
-    # d_sub - 1 fused multiply-adds, a compare, two selects, and one index move per pair plus
-    # one per four pairs of loop bookkeeping (gfx950 asm of encode_kernel)
-    enc_ops_per_pair = 2 * w.d_sub + 4.25
+    # VALU instructions per pair in the compiled scan (gfx950 asm of encode_kernel).  K a
+    # multiple of 64: d_sub subtractions, d_sub fused multiply-adds, a compare and two selects,
+    # plus a four-instruction merge per block of 64 centroids.  Other K: the same plus an index
+    # move per pair and loop bookkeeping per four pairs.
+    enc_ops_per_pair = 2 * w.d_sub + 3 + 4 / 64 if w.n_centroids % 64 == 0 else 2 * w.d_sub + 4.25
     enc_tops = enc_pairs * enc_ops_per_pair / (enc_total_ms * 1e-3) / 1e12
 
     result = {

@@ -8,10 +8,12 @@
 //
 // Work decomposition (gfx950): one work-group per (token block, kv head, sequence).
 // The head's codebook (K x d fp32, at most 128 KiB) is staged once into LDS; each
-// lane owns one token, keeps its d-element row in registers and scans all K
-// centroids of every subspace.  All lanes of a wave read the same centroid at the
-// same time, so the LDS reads are broadcasts.  The scan is plain fp32 VALU work:
-// (x - c)^2 summed over the subspace, strict '<' in ascending centroid order.
+// lane owns one token and walks its subspaces, holding one subvector (the next
+// one already requested) and scanning all K centroids for it.  All lanes of a
+// wave read the same centroid at the same time, so the LDS reads are broadcasts.
+// The scan is plain fp32 VALU work: (x - c)^2 summed over the subspace, strict '<'
+// in ascending centroid order; with K a multiple of 64 it costs 2*d_sub + 3
+// instructions per (subvector, centroid) pair (nearest_code).
 
 #include "nearest.h"
 
@@ -38,12 +40,22 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const int64_t i = (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
     if (i >= n_tokens) return;
 
-    float xv[D];
-    Row<XT>::template load<D>(x + b * s_seq + i * s_tok + h * s_head, xv);
-
+    // One subspace at a time: the next subvector is requested before the current
+    // one is scanned, so its latency hides behind K distance evaluations.
+    const XT* row = x + b * s_seq + i * s_tok + h * s_head;
     const int64_t t = t_start + i;
-    write_nearest_codes<D, DSUB>(xv, cbs, K, code_slot<M>(codes + ((int64_t)b * Hkv + h) * t_cap * M, t),
-                                 (int)(t & (kTileTokens - 1)));
+    uint8_t* dst = code_slot<M>(codes + ((int64_t)b * Hkv + h) * t_cap * M, t);
+    const int slot = (int)(t & (kTileTokens - 1));
+    float nxt[DSUB];
+    load_sub<DSUB>(row, nxt);
+#pragma unroll 1
+    for (int m = 0; m < M; ++m) {
+        float xs[DSUB];
+#pragma unroll
+        for (int j = 0; j < DSUB; ++j) xs[j] = nxt[j];
+        load_sub<DSUB>(row + (m + 1 < M ? m + 1 : m) * DSUB, nxt);
+        put_code<M>(dst, slot, m, nearest_code<DSUB, D>(xs, cbs + m * DSUB, K));
+    }
 }
 
 template <int D, int DSUB, typename XT>

@@ -52,16 +52,36 @@ def test_encode_matches_oracle(d, dsub, K, dtype):
         check_codes(got, x[s], cb, ref, d1, d2)
 
 
-def test_encode_duplicate_centroids_lowest_index():
-    d, dsub, K, H = 128, 2, 64, 2
+@pytest.mark.parametrize("K,keep,dups", [(64, 7, (40, 63)), (256, 70, (130, 200, 255)), (256, 7, (64, 100)),
+                                         (48, 5, (17, 47))])
+def test_encode_duplicate_centroids_lowest_index(K, keep, dups):
+    # exact ties, inside one block of 64 centroids and across blocks: the lowest index wins
+    d, dsub, H = 128, 2, 2
     M = d // dsub
     cb = _codebook(5, H, K, M, dsub)
-    cb[:, 40] = cb[:, 7]  # duplicates: index 7 must win
-    cb[:, 63] = cb[:, 7]
-    x = np.repeat(cb[:, 7][None], 70, axis=0).reshape(70, H, d).astype(np.float32)
+    for c in dups:
+        cb[:, c] = cb[:, keep]
+    x = np.repeat(cb[:, keep][None], 70, axis=0).reshape(70, H, d).astype(np.float32)
     planes = run_gpu_encode(dims_for(d, dsub, K, H, H), x[None], cb, 1, 128)
     got = oracle.untile_codes(planes[0], 70, M)
-    assert np.all(got == 7)
+    assert np.all(got == keep)
+
+
+@pytest.mark.parametrize("K", [256, 40])
+def test_encode_nan_and_inf_rows(K):
+    # a NaN subvector has no nearest centroid under '<': code 0, as in the oracle; an
+    # infinite one is at infinite distance from every centroid: code 0 as well
+    d, dsub, H = 64, 4, 1
+    M = d // dsub
+    cb = _codebook(6, H, K, M, dsub)
+    x = _outlier_values(7, (1, 64, H, d), np.float32)
+    x[0, 3, 0, 8] = np.nan
+    x[0, 9, 0, :] = np.inf
+    planes = run_gpu_encode(dims_for(d, dsub, K, H, H), x, cb, 1, 64)
+    got = oracle.untile_codes(planes[0], 64, M)
+    ref, _, _, _ = oracle.encode(x[0], cb)
+    assert got[0, 3, 2] == 0 and np.all(got[0, 9] == 0)
+    assert got[0, 3, 2] == ref[3, 0, 2] and np.array_equal(got[0, 9], ref[9, 0])
 
 
 def test_encode_deterministic():
