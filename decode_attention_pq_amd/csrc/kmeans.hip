@@ -38,15 +38,65 @@ __device__ inline float elem(const XT* p) {
         return *reinterpret_cast<const float*>(p);
 }
 
+// Nearest centroid of a point (its fp32 values widened to fp64), by the oracle's
+// rule: the running minimum starts at centroid 0 and moves only on a strictly
+// smaller distance, so the first minimum wins and NaN distances never win.  With
+// K a multiple of 16 the scan runs in unrolled blocks of 16 whose running index is
+// the block-relative position (an inline constant of the select); block 0 starts
+// from centroid 0's distance like the plain scan, later blocks from +inf, and a
+// block's winner replaces the running one only if strictly smaller, which picks
+// the same centroid as the plain scan.
 template <int DSUB>
-__device__ inline double sqdist(const float* x, const double* c) {
+__device__ __forceinline__ double sqdist_d(const double (&x)[DSUB], const double* c) {
     double s = 0.0;
 #pragma unroll
     for (int j = 0; j < DSUB; ++j) {
-        const double t = __dsub_rn((double)x[j], c[j]);
+        const double t = __dsub_rn(x[j], c[j]);
         s = __dadd_rn(s, __dmul_rn(t, t));
     }
     return s;
+}
+
+template <int DSUB>
+__device__ __forceinline__ int nearest_centroid(const double (&x)[DSUB], const double* C, int K) {
+    constexpr int BS = 16;  // centroids per unrolled block
+    if ((K & (BS - 1)) == 0) {
+        double best = 0.0;
+        int bi = 0;
+        for (int c0 = 0; c0 < K; c0 += BS) {
+            // block 0 starts from centroid 0's distance (which then never moves it)
+            double bb = c0 == 0 ? sqdist_d<DSUB>(x, C) : INFINITY;
+            int br = 0;
+            double cv[BS][DSUB];
+#pragma unroll
+            for (int r = 0; r < BS; ++r)
+#pragma unroll
+                for (int j = 0; j < DSUB; ++j) cv[r][j] = C[(c0 + r) * DSUB + j];
+#pragma unroll
+            for (int r = 0; r < BS; ++r) {
+                const double dc = sqdist_d<DSUB>(x, cv[r]);
+                if (dc < bb) {
+                    bb = dc;
+                    br = r;
+                }
+            }
+            if (c0 == 0 || bb < best) {
+                best = bb;
+                bi = c0 + br;
+            }
+        }
+        return bi;
+    }
+    int best = 0;
+    double bd = sqdist_d<DSUB>(x, C);
+    for (int c = 1; c < K; ++c) {
+        const double dc = sqdist_d<DSUB>(x, C + c * DSUB);
+        if (dc < bd) {
+            bd = dc;
+            best = c;
+        }
+    }
+    return best;
 }
 
 struct KmArgs {
@@ -113,17 +163,10 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_kernel(KmArgs a) {
     // ---- Lloyd iterations
     for (int it = 0; it < a.iters; ++it) {
         for (int64_t i = tid; i < n; i += kKmThreads) {
-            const float* p = pts + i * DSUB;
-            int best = 0;
-            double bd = sqdist<DSUB>(p, C);
-            for (int c = 1; c < K; ++c) {
-                const double dc = sqdist<DSUB>(p, C + c * DSUB);
-                if (dc < bd) {
-                    bd = dc;
-                    best = c;
-                }
-            }
-            asg[i] = (uint8_t)best;
+            double xd[DSUB];
+#pragma unroll
+            for (int j = 0; j < DSUB; ++j) xd[j] = (double)pts[i * DSUB + j];
+            asg[i] = (uint8_t)nearest_centroid<DSUB>(xd, C, K);
         }
         __syncthreads();
         // the update reads only assignments and points, so centroid c can be

@@ -134,6 +134,10 @@ DECODE_CASES = [
     (128, 2, 256, 2, 2, (100, 9000), (200, 3), 256, np.float16),
     (128, 2, 256, 3, 3, (4096, 0, 17, 12000, 4097, 8191), (1, 64, 0, 5, 64, 2), 64, np.float16),
     (128, 4, 256, 8, 2, (20000, 300, 0), (33, 0, 9), 64, np.float16),
+    # the largest recent window: 1024 rows in the one split of a short or empty history, and
+    # spread over the splits of a long one
+    (128, 2, 256, 2, 2, (100, 0), (1024, 1024), 1024, np.float16),
+    (64, 4, 256, 8, 2, (70000,), (1000,), 1024, np.float32),
 ]
 
 
