@@ -78,6 +78,8 @@ DecodePlan plan_decode(const pqkv_dims& d, int32_t batch, int64_t max_hist_len) 
         if (rounds < 1) rounds = 1;
         if (rounds > max_rounds) rounds = max_rounds;
         n_split = (max_hist_len + rounds * kTokensPerRound - 1) / (rounds * kTokensPerRound);
+        // the same number of splits, as even as whole rounds allow
+        rounds = (max_hist_len + n_split * kTokensPerRound - 1) / (n_split * kTokensPerRound);
         p.rounds = (int)rounds;
         p.n_split = (int)n_split;
         p.split_tokens = rounds * kTokensPerRound;

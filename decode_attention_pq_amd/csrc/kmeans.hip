@@ -38,9 +38,9 @@ __device__ inline float elem(const XT* p) {
         return *reinterpret_cast<const float*>(p);
 }
 
-// Nearest centroid of a point (its fp32 values widened to fp64), by the oracle's
-// rule: the running minimum starts at centroid 0 and moves only on a strictly
-// smaller distance, so the first minimum wins and NaN distances never win.  With
+// Nearest centroid of a point (its fp32 values widened to fp64), by the plain
+// scan's rule: the running minimum starts at centroid 0 and moves only on a
+// strictly smaller distance, so the first minimum wins and NaN distances never win.  With
 // K a multiple of 16 the scan runs in unrolled blocks of 16 whose running index is
 // the block-relative position (an inline constant of the select); block 0 starts
 // from centroid 0's distance like the plain scan, later blocks from +inf, and a
