@@ -235,7 +235,6 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     constexpr int RS = PQKV_MAX_RECENT;
     constexpr int P = kPrefetch;          // tiles in flight ahead of the one being used
     constexpr int NSLOT = P + 1;
-    constexpr int LUT_PER_THREAD = kLdsRows * M / kThreads;  // (centroid, subspace) pairs per thread
     constexpr int CPL = D / 64;                // epilogue: output components per lane
     constexpr int CPER = kLdsRows / kWaves;    // epilogue: centroids per wave
     constexpr int CHALF = CPER / 2;            // of which staged through LDS

@@ -1,5 +1,5 @@
-// Device helpers shared by the kernels that quantise head vectors: row loads and
-// the nearest-centroid scan of one token.
+// Device helpers shared by the kernels that quantise head vectors: subvector loads
+// and the nearest-centroid scan.
 //
 // MILLION write-up (DAC 2025), page "MILLION": the paragraph after Fig. 5 splits
 // the head vector into subspaces of dimension 2 or 4; the Fig. 6 paragraph
@@ -13,45 +13,6 @@
 #include "pqkv_internal.h"
 
 namespace pqkv {
-
-template <typename T>
-struct Row;
-
-template <>
-struct Row<float> {
-    template <int D>
-    __device__ static void load(const float* __restrict__ p, float (&v)[D]) {
-        const float4* p4 = reinterpret_cast<const float4*>(p);
-#pragma unroll
-        for (int i = 0; i < D / 4; ++i) {
-            float4 t = p4[i];
-            v[4 * i + 0] = t.x;
-            v[4 * i + 1] = t.y;
-            v[4 * i + 2] = t.z;
-            v[4 * i + 3] = t.w;
-        }
-    }
-};
-
-template <>
-struct Row<__half> {
-    template <int D>
-    __device__ static void load(const __half* __restrict__ p, float (&v)[D]) {
-        const uint4* p4 = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-        for (int i = 0; i < D / 8; ++i) {
-            uint4 t = p4[i];
-            const uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                __half2 h2 = *reinterpret_cast<const __half2*>(&w[k]);
-                float2 f = __half22float2(h2);
-                v[8 * i + 2 * k + 0] = f.x;
-                v[8 * i + 2 * k + 1] = f.y;
-            }
-        }
-    }
-};
 
 // Subvector loads: DSUB consecutive elements (DSUB = 2 or 4, naturally aligned)
 // as fp32.
