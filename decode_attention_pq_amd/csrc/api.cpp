@@ -70,16 +70,24 @@ DecodePlan plan_decode(const pqkv_dims& d, int32_t batch, int64_t max_hist_len) 
         p.n_split = 1;
         p.split_tokens = 0;
     } else {
-        const int max_rounds = decode_max_rounds(M, qh);
-        // enough splits to give every compute unit a work-group, then as few
-        // rounds per wave as that allows
-        int64_t n_split = (kPlanCUs + p.units - 1) / p.units;
-        int64_t rounds = (max_hist_len + n_split * kTokensPerRound - 1) / (n_split * kTokensPerRound);
-        if (rounds < 1) rounds = 1;
-        if (rounds > max_rounds) rounds = max_rounds;
-        n_split = (max_hist_len + rounds * kTokensPerRound - 1) / (rounds * kTokensPerRound);
-        // the same number of splits, as even as whole rounds allow
-        rounds = (max_hist_len + n_split * kTokensPerRound - 1) / (n_split * kTokensPerRound);
+        // Enough splits to give every compute unit a work-group, then as few splits
+        // (as many rounds per wave, up to cap) as that allows, cut evenly.  A
+        // work-group's fixed costs (codebooks, LUT, epilogue, merge) outweigh a round
+        // of streaming, so longer splits win once every CU is busy.
+        const int64_t per_tok = kTokensPerRound;
+        int64_t n_split = 0, rounds = 0;
+        auto fit = [&](int cap) {
+            n_split = (kPlanCUs + p.units - 1) / p.units;
+            rounds = (max_hist_len + n_split * per_tok - 1) / (n_split * per_tok);
+            if (rounds < 1) rounds = 1;
+            if (rounds > cap) rounds = cap;
+            n_split = (max_hist_len + rounds * per_tok - 1) / (rounds * per_tok);
+            rounds = (max_hist_len + n_split * per_tok - 1) / (n_split * per_tok);
+        };
+        fit(decode_max_rounds(M, qh));
+        // the 64-subspace kernel runs 9..11 rounds in its 16-round build, whose unused
+        // steps cost more than the extra splits of the 8-round build
+        if (M == 64 && rounds > 8 && rounds < 12) fit(8);
         p.rounds = (int)rounds;
         p.n_split = (int)n_split;
         p.split_tokens = rounds * kTokensPerRound;

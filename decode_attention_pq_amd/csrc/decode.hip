@@ -32,7 +32,9 @@
 //     work-group max is taken once, then p = exp2(s - max) is added into the
 //     histogram.  The adds are u32 fixed point (round(p * 2^S)): on gfx950 an
 //     fp32 LDS add serialises the wave (~190 clk per instruction) while the u32
-//     add takes ~4 clk.  S is chosen so that no histogram cell can overflow.
+//     add takes ~4 clk.  S comes from a bound on the split's weight sum (taken
+//     with the max), as large as keeps every cell inside u32, so the rounding is
+//     relative to the sum of the weights.
 //   - Each work-group also takes a slice of the recent window (exact fp32 dot
 //     products), writes its partial (max, sum, unnormalised output), and the
 //     last work-group of a (sequence, kv head, group) to finish merges all
@@ -218,8 +220,6 @@ struct DecArgs {
     const void* rv;
     int64_t r_cap;
     float scale_log2;
-    float fix_scale;  // 2^S
-    float fix_inv;    // 2^-S
     int pstride;
     float* partials;
     uint32_t* counters;
@@ -227,11 +227,11 @@ struct DecArgs {
     float* lse;
 };
 
-template <int M, int DSUB, int QH, typename QT, typename RT>
+template <int M, int DSUB, int QH, int RW, typename QT, typename RT>
 __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     constexpr int D = M * DSUB;
     constexpr int NCH = M / 16;
-    constexpr int RW = decode_max_rounds(M, QH);
+    static_assert(RW >= 1 && RW <= decode_max_rounds(M, QH), "tiles per wave beyond the register budget");
     constexpr int RS = PQKV_MAX_RECENT;
     constexpr int P = kPrefetch;          // tiles in flight ahead of the one being used
     constexpr int NSLOT = P + 1;
@@ -245,7 +245,9 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     __shared__ float lds[2 * kLdsRows * kRow];
     __shared__ float ored[kWaves * QH * D];     // per-wave output partials
     __shared__ float rs[QH * RS];               // recent scores, then weights * 2^S
-    __shared__ float red[kWaves * QH];
+    __shared__ float red[kWaves * QH];   // per-wave maxima
+    __shared__ float redl[kWaves * QH];  // per-wave bounds on the history weight sums
+    __shared__ float redr[kWaves * QH];  // per-wave recent weight sums
     __shared__ uint32_t redu[kWaves * QH];
     __shared__ int last_flag;
     uint32_t* hist = reinterpret_cast<uint32_t*>(lds);
@@ -488,15 +490,24 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         }
     }
 
-    // ---- 4. work-group max over history and recent scores
+    // ---- 4. work-group max over history and recent scores, and a bound on the
+    //         history's weight sum, which sets the histogram's fixed-point scale: a
+    //         lane's RW weights sum to at most RW times its largest.  Each wave takes
+    //         the bound against its own max; the waves' bounds meet after the barrier.
 #pragma unroll
     for (int j = 0; j < QH; ++j) {
-        float v = -INFINITY;
+        float vl = -INFINITY;
 #pragma unroll
-        for (int s = 0; s < RW; ++s) v = fmaxf(v, sc[s][j]);
+        for (int s = 0; s < RW; ++s) vl = fmaxf(vl, sc[s][j]);
+        float v = vl;
         for (int i = tid; i < n_rec; i += kThreads) v = fmaxf(v, rs[j * RS + i]);
         v = wave_max(v);
-        if (lane == 0) red[wave * QH + j] = v;
+        float l = vl != -INFINITY ? (float)RW * exp2f(vl - v) : 0.0f;
+        l = wave_sum(l);
+        if (lane == 0) {
+            red[wave * QH + j] = v;
+            redl[wave * QH + j] = l;
+        }
     }
     __syncthreads();
     float mx[QH];
@@ -547,6 +558,30 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 #pragma unroll
         for (int t = 0; t < CPL; ++t) vpre[p][t] = to_f32(row[i < n_rec ? t : 0]);
     }
+    // Fixed point: the history weights p = 2^(s - max) are added to the histogram as
+    // round(p * 2^S), S the largest with L * 2^S < 2^31 for the bound L on the split's
+    // weight sum (capped at 64).  A cell, and the split's sum, then stay below 2^31
+    // plus half a unit per token, inside u32, and each weight is exact to 2^-(S+1),
+    // i.e. to L * 2^-32 with L at most RW times the true sum: the rounding is
+    // relative to the sum of the weights, not to the largest one.
+    // (Taken after the value-codebook requests, whose latency it overlaps.)
+    float fs[QH], fi[QH];
+#pragma unroll
+    for (int j = 0; j < QH; ++j) {
+        const float v = mx[j];
+        float L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float m = red[w * QH + j];
+            if (m != -INFINITY) L += redl[w * QH + j] * exp2f(m - v);
+        }
+        // L = f * 2^e with f in [0.5, 1): S = 31 - e (normal L; 64 for zero or tiny L)
+        const int e = (int)((__float_as_uint(L) >> 23) & 0xffu) - 126;
+        int S = L >= 1.0e-30f ? 31 - e : 64;
+        S = S < 0 ? 0 : (S > 64 ? 64 : S);
+        fs[j] = __uint_as_float((uint32_t)(127 + S) << 23);
+        fi[j] = __uint_as_float((uint32_t)(127 - S) << 23);
+    }
     // byte s of mw[k] = 4 * ((4k + s + slot) mod M): subspace byte offsets
     uint32_t mw[M / 4];
 #pragma unroll
@@ -567,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
             uint32_t p[QH];
 #pragma unroll
             for (int j = 0; j < QH; ++j) {
-                p[j] = __float2uint_rn(exp2f(sc[s - RW][j] - mx[j]) * a.fix_scale);
+                p[j] = __float2uint_rn(exp2f(sc[s - RW][j] - mx[j]) * fs[j]);
                 lsum[j] += p[j];
             }
 #pragma unroll
@@ -597,14 +632,14 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     for (int j = 0; j < QH; ++j) {
         float l = 0.0f;
         for (int i = tid; i < n_rec; i += kThreads) {
-            const float p = exp2f(rs[j * RS + i] - mx[j]) * a.fix_scale;
+            const float p = exp2f(rs[j * RS + i] - mx[j]) * fs[j];
             rs[j * RS + i] = p;
             l += p;
         }
         l = wave_sum(l);
         const uint32_t lh = wave_sum_u32(lsum[j]);
         if (lane == 0) {
-            red[wave * QH + j] = l;
+            redr[wave * QH + j] = l;
             redu[wave * QH + j] = lh;
         }
     }
@@ -687,7 +722,10 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) s += ored[w * QH * D + e];
         const int j = e / D;
-        publish(part + j * head_step + (e - j * D), s * a.fix_inv);
+        float inv = fi[0];
+#pragma unroll
+        for (int q = 1; q < QH; ++q) inv = j == q ? fi[q] : inv;
+        publish(part + j * head_step + (e - j * D), s * inv);
     }
     if (tid < QH) {
         uint32_t lh = 0u;
@@ -695,10 +733,16 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             lh += redu[w * QH + tid];
-            lr += red[w * QH + tid];
+            lr += redr[w * QH + tid];
         }
-        publish(part + tid * head_step + D, any ? mx[tid] : -INFINITY);
-        publish(part + tid * head_step + D + 1, ((float)lh + lr) * a.fix_inv);
+        float m = mx[0], inv = fi[0];
+#pragma unroll
+        for (int q = 1; q < QH; ++q) {
+            m = tid == q ? mx[q] : m;
+            inv = tid == q ? fi[q] : inv;
+        }
+        publish(part + tid * head_step + D, any ? m : -INFINITY);
+        publish(part + tid * head_step + D + 1, ((float)lh + lr) * inv);
     }
 
     // ---- 7. the last work-group of this unit merges every split's partial.
@@ -761,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     if (tid == 0) __hip_atomic_store(a.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int M, int DSUB, int QH, typename QT, typename RT>
+template <int M, int DSUB, int QH, int RW, typename QT, typename RT>
 hipError_t launch_typed(const pqkv_dims& d, int32_t batch, const DecodePlan& plan, const DecodeArgs& in,
                         hipStream_t stream) {
     DecArgs k;
@@ -778,12 +822,6 @@ hipError_t launch_typed(const pqkv_dims& d, int32_t batch, const DecodePlan& pla
     k.r_cap = in.r_cap;
     k.recent_len = in.recent_len;
     k.scale_log2 = in.scale_log2;
-    // Largest S with split_tokens * 2^S <= 2^31: a histogram cell and the weight sum
-    // stay below 2^31 even if every token had weight 1.
-    int S = 31;
-    for (int64_t t = plan.split_tokens; t > 1; t = (t + 1) / 2) --S;
-    k.fix_scale = ldexpf(1.0f, S);
-    k.fix_inv = ldexpf(1.0f, -S);
     k.partials = in.partials;
     k.counters = in.counters;
     k.out = in.out;
@@ -799,7 +837,7 @@ hipError_t launch_typed(const pqkv_dims& d, int32_t batch, const DecodePlan& pla
     k.split_tokens = plan.split_tokens;
     const int64_t items = (int64_t)batch * d.n_kv_heads * plan.n_groups * plan.n_split;
     k.n_items = (int)items;
-    hipLaunchKernelGGL((pq_decode_kernel<M, DSUB, QH, QT, RT>), dim3((unsigned)items), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((pq_decode_kernel<M, DSUB, QH, RW, QT, RT>), dim3((unsigned)items), dim3(kThreads), 0, stream,
                        k);
     return hipGetLastError();
 }
@@ -808,12 +846,16 @@ template <int M, int DSUB, typename QT, typename RT>
 hipError_t launch_qh(const pqkv_dims& d, int32_t batch, const DecodePlan& plan, const DecodeArgs& a,
                      hipStream_t stream) {
     if constexpr (M <= 16) {
-        if (plan.qh == 4) return launch_typed<M, DSUB, 4, QT, RT>(d, batch, plan, a, stream);
+        if (plan.qh == 4) return launch_typed<M, DSUB, 4, decode_max_rounds(M, 4), QT, RT>(d, batch, plan, a, stream);
     }
     if constexpr (M <= 32) {
-        if (plan.qh == 2) return launch_typed<M, DSUB, 2, QT, RT>(d, batch, plan, a, stream);
+        if (plan.qh == 2) return launch_typed<M, DSUB, 2, decode_max_rounds(M, 2), QT, RT>(d, batch, plan, a, stream);
     }
-    return launch_typed<M, DSUB, 1, QT, RT>(d, batch, plan, a, stream);
+    if constexpr (M == 64) {
+        if (decode_kernel_rounds(M, 1, plan.rounds) == 8)
+            return launch_typed<M, DSUB, 1, 8, QT, RT>(d, batch, plan, a, stream);
+    }
+    return launch_typed<M, DSUB, 1, decode_max_rounds(M, 1), QT, RT>(d, batch, plan, a, stream);
 }
 
 template <typename QT, typename RT>

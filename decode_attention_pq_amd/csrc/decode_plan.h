@@ -18,9 +18,15 @@ constexpr int kPlanCUs = 256;         // MI355X compute units the split plan fil
 constexpr int kLdsRows = 256;         // LDS table rows (any uint8 code stays in bounds)
 
 // Tiles per wave in one decode split: each tile's scores stay in registers until
-// the split's softmax max is known, and the fully unrolled tile loop of the
-// kernel (rounds x M code bytes per lane) stays well inside the instruction cache.
-constexpr int decode_max_rounds(int n_sub, int qh) { return (n_sub == 64 || qh == 4) ? 8 : 16; }
+// the split's softmax max is known, and the fully unrolled tile loop fits the
+// register budget.
+constexpr int decode_max_rounds(int n_sub, int qh) { return qh == 4 ? 8 : 16; }
+// Tiles per wave a kernel build unrolls.  Steps past the plan's rounds still issue
+// their (dummy) loads, so the 64-subspace kernel, whose splits run 8 rounds when
+// every CU gets one, also comes in an 8-round build.
+constexpr int decode_kernel_rounds(int n_sub, int qh, int rounds) {
+    return (n_sub == 64 && rounds <= 8) ? 8 : decode_max_rounds(n_sub, qh);
+}
 // Splits per unit the merge can take (its split maxima and sums live in LDS).
 constexpr int kMaxSplits = 512;
 

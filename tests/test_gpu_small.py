@@ -245,3 +245,34 @@ def test_two_step_decode_merges_like_one():
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, [T], rk, rv, [R], scale)
     check_attention(out.cpu().numpy()[None], lse.cpu().numpy()[None], ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("hist", [8192, 4096])
+def test_decode_many_small_weights_are_kept(hist):
+    """One token outweighs each of the others by about 2^20.5, and the others together
+    carry ~0.5% of the attention.  Their weights must survive the histogram's fixed
+    point: dropping them moves the output by ~1%, five times the tolerance.  Splits of
+    4096 and 8192 tokens (one split per sequence: 8 x 32 = 256 units fill the CUs)."""
+    d, dsub, K, H, B = 128, 2, 16, 32, 8
+    M = d // dsub
+    t_cap = hist
+    top = 2917  # the heavy token
+    cbk = np.zeros((H, K, M, dsub), np.float32)
+    cbk[:, 1, :, 0] = 1.0
+    cbv = np.zeros((H, K, M, dsub), np.float32)
+    cbv[:, 0] = 1.0
+    cbv[:, 1] = -1.0
+    ck = np.zeros((B, H, t_cap, M), np.uint8)
+    ck[:, :, top] = 1
+    cv = ck.copy()
+    scale = softmax_scale(d)
+    # score gap scale * M * q: 20.5 bits in the log2 domain
+    q = np.zeros((B, H, d), np.float16)
+    q[:, :, 0::2] = np.float16(20.5 * np.log(2.0) / (scale * M))
+    rk = rv = np.zeros((B, H, 0, d), np.float16)
+    ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, [hist] * B, rk, rv, [0] * B, scale)
+    assert np.all(np.abs(ref_out + 1.0) > 5e-3), "the small weights must matter"
+    pk, pv = oracle.tile_codes(ck, t_cap), oracle.tile_codes(cv, t_cap)
+    out, lse = run_gpu_decode(dims_for(d, dsub, K, H, H), q, cbk, cbv, pk, pv, t_cap, [hist] * B, None, None,
+                              [0] * B, scale)
+    check_attention(out, lse, ref_out, ref_lse)
