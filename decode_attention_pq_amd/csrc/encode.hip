@@ -20,7 +20,7 @@
 namespace pqkv {
 namespace {
 
-constexpr int kEncThreads = 512;
+constexpr int kEncThreads = 1024;
 
 template <int D, int DSUB, typename XT>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(

@@ -70,9 +70,9 @@ __device__ inline int nearest_code(const float (&xs)[DSUB], const float* cm, int
     float best = INFINITY;
     int bi = 0;
     if ((K & 63) == 0) {
-        // centroid values are read in groups of G (128 floats in registers) before
+        // centroid values are read in groups of G (64 floats in registers) before
         // the group's distances, so the LDS latency is paid once per group
-        constexpr int G = 128 / DSUB;
+        constexpr int G = 64 / DSUB;
         for (int c0 = 0; c0 < K; c0 += 64) {
             const float* cb = cm + c0 * CS;
             float bb = INFINITY;
