@@ -510,13 +510,36 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         }
     }
     __syncthreads();
-    float mx[QH];
+    // Fixed point: the history weights p = 2^(s - max) are added to the histogram as
+    // round(p * 2^S), S the largest with L * 2^S < 2^31 for the bound L on the split's
+    // weight sum (capped at 64).  A cell, and the split's sum, then stay below 2^31
+    // plus half a unit per token, inside u32, and each weight is exact to 2^-(S+1),
+    // i.e. to L * 2^-32 with L at most RW times the true sum: the rounding is
+    // relative to the sum of the weights, not to the largest one.
+    float mx[QH], fs[QH], fi[QH];
 #pragma unroll
     for (int j = 0; j < QH; ++j) {
+        float mw[kWaves], lw[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            mw[w] = red[w * QH + j];
+            lw[w] = redl[w * QH + j];
+        }
         float v = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) v = fmaxf(v, red[w * QH + j]);
+        for (int w = 0; w < kWaves; ++w) v = fmaxf(v, mw[w]);
+        // a wave without tokens has max -inf and adds 2^-inf = 0 (its bound is finite)
+        float L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) L = fmaf(lw[w], exp2f(mw[w] - v), L);
+        if (v == -INFINITY) L = 0.0f;
         mx[j] = v;
+        // L = f * 2^e with f in [0.5, 1): S = 31 - e (normal L; 64 for zero or tiny L)
+        const int e = (int)((__float_as_uint(L) >> 23) & 0xffu) - 126;
+        int S = L >= 1.0e-30f ? 31 - e : 64;
+        S = S < 0 ? 0 : (S > 64 ? 64 : S);
+        fs[j] = __uint_as_float((uint32_t)(127 + S) << 23);
+        fi[j] = __uint_as_float((uint32_t)(127 - S) << 23);
     }
     const bool any = mx[0] != -INFINITY;  // the split holds at least one token (all heads alike)
 
@@ -557,30 +580,6 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         const RT* row = i < n_rec ? rv + (int64_t)i * D + em * DSUB + ecomp : rzero;
 #pragma unroll
         for (int t = 0; t < CPL; ++t) vpre[p][t] = to_f32(row[i < n_rec ? t : 0]);
-    }
-    // Fixed point: the history weights p = 2^(s - max) are added to the histogram as
-    // round(p * 2^S), S the largest with L * 2^S < 2^31 for the bound L on the split's
-    // weight sum (capped at 64).  A cell, and the split's sum, then stay below 2^31
-    // plus half a unit per token, inside u32, and each weight is exact to 2^-(S+1),
-    // i.e. to L * 2^-32 with L at most RW times the true sum: the rounding is
-    // relative to the sum of the weights, not to the largest one.
-    // (Taken after the value-codebook requests, whose latency it overlaps.)
-    float fs[QH], fi[QH];
-#pragma unroll
-    for (int j = 0; j < QH; ++j) {
-        const float v = mx[j];
-        float L = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float m = red[w * QH + j];
-            if (m != -INFINITY) L += redl[w * QH + j] * exp2f(m - v);
-        }
-        // L = f * 2^e with f in [0.5, 1): S = 31 - e (normal L; 64 for zero or tiny L)
-        const int e = (int)((__float_as_uint(L) >> 23) & 0xffu) - 126;
-        int S = L >= 1.0e-30f ? 31 - e : 64;
-        S = S < 0 ? 0 : (S > 64 ? 64 : S);
-        fs[j] = __uint_as_float((uint32_t)(127 + S) << 23);
-        fi[j] = __uint_as_float((uint32_t)(127 - S) << 23);
     }
     // byte s of mw[k] = 4 * ((4k + s + slot) mod M): subspace byte offsets
     uint32_t mw[M / 4];
