@@ -311,6 +311,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     //         centroids c = (t + k*512) / (M/EPL), from one 16-byte load each.
     constexpr int EPL = 4 / DSUB;
     constexpr int LUT_LOADS = kLdsRows * M / EPL / kThreads;
+    static_assert(LUT_LOADS * kThreads == kLdsRows * (M / EPL), "the LUT loads cover the table rows exactly");
     const int mg = tid % (M / EPL);
     const QT* qrow = static_cast<const QT*>(a.q) + (int64_t)(b * a.Hq + hq0) * D;
     float ql[QH][4];       // q elements [4*mg, 4*mg + 4) of each head, for the LUT
@@ -388,9 +389,10 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     for (int s = 0; s < P; ++s) issue(ring[s], s);
 
     // zero the histogram now, while the codebook is on its way (phase 1 reads only the
-    // LUT region; the barrier before phase 1 orders these stores before any atomic)
+    // LUT region; the barrier before phase 1 orders these stores before any atomic).
+    // All rows: those past K stay 0, so the epilogue reads them without a check.
     if (has_hist)
-        for (int e = tid; e < K * kRow / 4; e += kThreads)
+        for (int e = tid; e < kLdsRows * kRow / 4; e += kThreads)
             reinterpret_cast<uint4*>(hist)[e] = make_uint4(0u, 0u, 0u, 0u);
 
     // ---- 2. ad-LUT in LDS, recent-window scores, per-lane subspace offsets
@@ -404,18 +406,17 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     if (has_hist) {
 #pragma unroll
         for (int k = 0; k < LUT_LOADS; ++k) {
+            // c < kLdsRows always; rows past K hold copies of row K-1 that no code reads
             const int c = (tid + lut_block(k) * kThreads) / (M / EPL);
-            if (c < K) {
-                const float cv[4] = {cbq[k].x, cbq[k].y, cbq[k].z, cbq[k].w};
+            const float cv[4] = {cbq[k].x, cbq[k].y, cbq[k].z, cbq[k].w};
 #pragma unroll
-                for (int j = 0; j < QH; ++j) {
+            for (int j = 0; j < QH; ++j) {
 #pragma unroll
-                    for (int t = 0; t < EPL; ++t) {
-                        float s = 0.0f;
+                for (int t = 0; t < EPL; ++t) {
+                    float s = 0.0f;
 #pragma unroll
-                        for (int i = 0; i < DSUB; ++i) s = fmaf(ql[j][t * DSUB + i], cv[t * DSUB + i], s);
-                        table[c * kRow + j * M + mg * EPL + t] = s;
-                    }
+                    for (int i = 0; i < DSUB; ++i) s = fmaf(ql[j][t * DSUB + i], cv[t * DSUB + i], s);
+                    table[c * kRow + j * M + mg * EPL + t] = s;
                 }
             }
         }
@@ -659,15 +660,15 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
                 // direct-to-LDS loads are not tracked by the compiler's waits)
                 __builtin_amdgcn_s_waitcnt(0);
                 __builtin_amdgcn_sched_barrier(0);
-                // histogram reads in groups of 8 (rows past K read a valid row and count
-                // 0), so the LDS latency is paid once per group
+                // histogram reads in groups of 8, so the LDS latency is paid once per group
+                // (rows past K hold 0 and meet zero or finite value rows)
 #pragma unroll
                 for (int k0 = 0; k0 < CPER; k0 += 8) {
                     uint32_t hv[8][QH];
                     float cv[8][CPL];
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
-                        const int c = ec0 + k0 + k < K ? ec0 + k0 + k : K - 1;
+                        const int c = ec0 + k0 + k;
 #pragma unroll
                         for (int j = 0; j < QH; ++j) hv[k][j] = hist[c * kRow + j * M + em];
 #pragma unroll
@@ -677,10 +678,9 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
                     }
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
-                        const bool live = ec0 + k0 + k < K;
 #pragma unroll
                         for (int j = 0; j < QH; ++j) {
-                            const float w = live ? (float)hv[k][j] : 0.0f;
+                            const float w = (float)hv[k][j];
 #pragma unroll
                             for (int i = 0; i < CPL; ++i) acc[j][i] = fmaf(w, cv[k][i], acc[j][i]);
                         }
