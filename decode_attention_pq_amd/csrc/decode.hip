@@ -177,7 +177,7 @@ template <int NCH>
 __device__ inline void load_tile(u32x4 (&cw)[NCH], const uint8_t* __restrict__ plane, int64_t tile, int lane,
                                  bool ok) {
     const uint8_t* p = ok ? plane + tile * (kTileTokens * NCH * 16) : reinterpret_cast<const uint8_t*>(g_zero_block);
-    p += lane * 16;
+    p += ok ? lane * 16 : 0;  // an unused slot reads one 16-byte line
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
         cw[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + c * (kTileTokens * 16)));
