@@ -21,13 +21,15 @@
 //     tokens -- keeping three tiles in flight ahead of the one in use.  The
 //     codebook values for the LUT are requested before the first tiles, because
 //     vector-memory loads of a wave retire in issue order.
-//   - LDS holds the ad-LUT of the work-group's QH query heads (bytes 0..64K) and
-//     a u32 histogram of the same shape (bytes 64K..128K): row c = centroid c,
-//     entry j*M + m = (query head j, subspace m).  The code-cache layout rotates
-//     each token's bytes by its slot, so at every step the 64 lanes address 64
-//     different subspaces and the LDS accesses never conflict; one v_perm_b32
-//     per code forms the byte address (code << 8) | (4*m), plus 0x10000 for the
-//     histogram.
+//   - LDS holds a u32 histogram (bytes 0..64K) and the ad-LUT of the
+//     work-group's QH query heads (bytes 64K..128K), both with row c = centroid
+//     c and entry j*M + m = (query head j, subspace m).  The code-cache layout
+//     rotates each token's bytes by its slot, so at every step the 64 lanes
+//     address 64 different subspaces and the LDS accesses never conflict; one
+//     v_perm_b32 per code forms the byte address (code << 8) | (4*m), plus
+//     0x10000 for the LUT.
+//   - A wave's tiles per split (RW, 8 or 16) are a template parameter: their
+//     scores stay in registers until the work-group max is known.
 //   - Two-phase softmax inside the work-group: scores stay in registers, the
 //     work-group max is taken once, then p = exp2(s - max) is added into the
 //     histogram.  The adds are u32 fixed point (round(p * 2^S)): on gfx950 an
@@ -807,6 +809,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 template <int M, int DSUB, int QH, int RW, typename QT, typename RT>
 hipError_t launch_typed(const pqkv_dims& d, int32_t batch, const DecodePlan& plan, const DecodeArgs& in,
                         hipStream_t stream) {
+    if (plan.rounds > RW) return hipErrorInvalidValue;  // the build must unroll every round
     DecArgs k;
     k.q = in.q;
     k.cb_k = in.cb_k;
