@@ -138,6 +138,13 @@ DECODE_CASES = [
     # spread over the splits of a long one
     (128, 2, 256, 2, 2, (100, 0), (1024, 1024), 1024, np.float16),
     (64, 4, 256, 8, 2, (70000,), (1000,), 1024, np.float32),
+    # enough (sequence, head) units to fill the CUs with one split each: 13 rounds per wave
+    # in the 16-round build (three unused steps), ragged and empty rows among them
+    (128, 2, 64, 32, 32, (6500, 100, 0, 6144, 6145, 3000, 6600, 5000), (3,) * 8, 8, np.float16),
+    # 10 rounds would be needed: the plan takes two splits of 5 rounds in the 8-round build
+    (128, 2, 256, 32, 32, (5000, 4999, 1, 2500, 5000, 4097, 64, 4096), (0, 1, 2, 3, 4, 5, 6, 7), 8, np.float16),
+    # d_sub 4, two query heads per work-group, 10 rounds in the 16-round build
+    (128, 4, 256, 32, 8, (20000, 19000, 300, 20000), (5, 0, 9, 2), 16, np.float16),
 ]
 
 
