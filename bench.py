@@ -254,6 +254,15 @@ def main():
     per_call_us = sorted(a.elapsed_time(b) * 1e3 / calls_per_step for a, b in evs)
     pct = lambda p: round(per_call_us[min(len(per_call_us) - 1, int(p * len(per_call_us)))], 3)
 
+    # the output the CPU leg checks: one more call on copy 0, outside the timed region
+    check = None
+    if calls_per_step == 1 and not args.no_cpu:
+        c0 = copies[0]
+        call(c0)
+        torch.cuda.synchronize()
+        check = {k: c0[k].cpu().numpy() for k in ("q", "cbk", "cbv", "ck", "cv", "rk", "rv")}
+        check["out"], check["lse"] = out.cpu().numpy(), lse.cpu().numpy()
+
     # the live-cache step: one new row per sequence, with and without a roll into the history
     append_us = None
     if calls_per_step == 1 and R > 1:
@@ -344,7 +353,8 @@ def main():
                    "achieved": round(enc_tops, 2), "peak": round(VALU_LANE_OPS_PEAK_T, 2), "unit": "T VALU lane-ops/s",
                    "frac": round(enc_tops / VALU_LANE_OPS_PEAK_T, 4),
                    "flop_form_tflops": round(enc_tflops, 2), "fp32_peak_tflops": FP32_VALU_PEAK_TFLOPS,
-                   "hbm_gbs": round(encode_bytes(w, enc_tokens // 2) / (enc_total_ms * 1e-3) / 1e9, 1)},
+                   "hbm_gbs": round(encode_bytes(w, enc_tokens // 2) / (enc_total_ms * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(encode_bytes(w, enc_tokens // 2) / (enc_total_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     if fit is not None:
         result["fit_codebooks"] = fit
@@ -362,41 +372,67 @@ def main():
         del src, dst
 
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"], parity = cpu_baseline(w, args.cpu_seconds, check)
+        if parity is not None:
+            result["parity"] = parity
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, target_s):
+def cpu_baseline(w, target_s, check=None):
     """The CPU oracle (fp64 dequantise-then-exact attention) on a sample of the same workload:
-    the first few kv heads of the 32K layer, with seeded random codes.  Scaled to the
-    whole call by the head count."""
+    the first kv heads (and their query heads) of sequence 0, scaled to the whole call by the
+    head count.  With `check` (copy 0's inputs and the GPU's output for them) the sample is
+    that copy's real codes and the oracle's result is compared with the GPU's, at the
+    attention tolerance (2e-3, row-normwise); otherwise seeded random codes stand in."""
     import oracle
     import synthkv
 
     d, M, K = w.head_dim, w.n_sub, w.n_centroids
-    T, R = w.max_hist, w.recent_len
-    h_s = 4
-    rng_q = synthkv.queries(w)[:, :h_s]
-    cbk = synthkv.drawn_codebook(w, 0, "k")[:h_s]
-    cbv = synthkv.drawn_codebook(w, 0, "v")[:h_s]
-    ck = synthkv.small_codes(7, (1, h_s, T, M), K)
-    cv = synthkv.small_codes(8, (1, h_s, T, M), K)
-    rk = synthkv.recent_kv(w, 0, "k")[:, :h_s]
-    rv = synthkv.recent_kv(w, 0, "v")[:, :h_s]
+    g = w.n_q_heads // w.n_kv_heads
+    R = w.recent_len
+    hk = min(4, w.n_kv_heads)
+    hq = hk * g
     scale = float(np.float32(1.0 / math.sqrt(d)))
+    if check is not None:
+        T = int(w.hist_len[0])
+        q = check["q"][:1, :hq]
+        cbk, cbv = check["cbk"][:hk], check["cbv"][:hk]
+        ck = oracle.untile_codes(check["ck"][0, :hk], T, M)[None]
+        cv = oracle.untile_codes(check["cv"][0, :hk], T, M)[None]
+        rk, rv = check["rk"][:1, :hk], check["rv"][:1, :hk]
+    else:
+        T = w.max_hist
+        q = synthkv.queries(w)[:1, :hq]
+        cbk = synthkv.drawn_codebook(w, 0, "k")[:hk]
+        cbv = synthkv.drawn_codebook(w, 0, "v")[:hk]
+        ck = synthkv.small_codes(7, (1, hk, T, M), K)
+        cv = synthkv.small_codes(8, (1, hk, T, M), K)
+        rk = synthkv.recent_kv(w, 0, "k")[:1, :hk]
+        rv = synthkv.recent_kv(w, 0, "v")[:1, :hk]
     t0 = time.time()
     reps = 0
     while True:
-        oracle.decode_exact(rng_q, cbk, cbv, ck, cv, [T], rk, rv, [R], scale)
+        ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, [T], rk, rv, [R], scale)
         reps += 1
         if time.time() - t0 >= target_s:
             break
     el = time.time() - t0
-    per_call = el / reps * (w.n_q_heads / h_s)
-    return {"value": round((T + R) / per_call, 1), "unit": "KV tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"{reps} x fp64 dequantise-then-exact attention over {h_s} of {w.n_q_heads} heads "
-                      f"({T}+{R} tokens), scaled to all heads; {el:.1f}s"}
+    per_call = el / reps * (w.n_q_heads / hq)
+    baseline = {"value": round((T + R) / per_call, 1), "unit": "KV tokens/s", "cores": oracle.max_threads(),
+                "kind": "oracle",
+                "sample": f"{reps} x fp64 dequantise-then-exact attention over {hq} of {w.n_q_heads} query heads "
+                          f"of sequence 0 ({T}+{R} tokens, {'copy 0 of the timed inputs' if check else 'random codes'}),"
+                          f" scaled to all heads; {el:.1f}s"}
+    parity = None
+    if check is not None:
+        got, got_lse = check["out"][0, :hq].astype(np.float64), check["lse"][0, :hq].astype(np.float64)
+        ref, ref_l = ref_out[0], ref_lse[0]
+        row = np.max(np.abs(got - ref), axis=-1) / np.maximum(np.max(np.abs(ref), axis=-1), 1e-6)
+        lerr = np.abs(got_lse - ref_l) / np.maximum(1.0, np.abs(ref_l))
+        parity = {"what": f"GPU output of copy 0 against the oracle, {hq} query heads of sequence 0",
+                  "max_row_rel_err": float(row.max()), "max_lse_rel_err": float(lerr.max()), "tol": 2e-3,
+                  "ok": bool(row.max() <= 2e-3 and lerr.max() <= 2e-3)}
+    return baseline, parity
 
 
 if __name__ == "__main__":
