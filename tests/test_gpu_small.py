@@ -283,3 +283,26 @@ def test_decode_many_small_weights_are_kept(hist):
     out, lse = run_gpu_decode(dims_for(d, dsub, K, H, H), q, cbk, cbv, pk, pv, t_cap, [hist] * B, None, None,
                               [0] * B, scale)
     check_attention(out, lse, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("B,H,hist", [(8, 32, 8192), (8, 32, 4096), (1, 2, 70000)])
+def test_decode_identical_tokens_fill_one_cell(B, H, hist):
+    """Every history token has the same K and V codes: all weights are equal and each
+    (centroid, subspace) histogram cell of a split takes every token of it -- the largest
+    a cell can get.  The result is the selected value centroids exactly, lse = s + ln T."""
+    d, dsub, K = 128, 2, 4
+    M = d // dsub
+    t_cap = -(-hist // 64) * 64
+    cbk = _codebook(11, H, K, M, dsub, 1.0)
+    cbv = _codebook(12, H, K, M, dsub, 1.0)
+    ck = np.full((B, H, t_cap, M), 1, np.uint8)
+    cv = np.full((B, H, t_cap, M), 2, np.uint8)
+    q = synthkv.small_normal(13, (B, H, d), np.float16)
+    rk = rv = np.zeros((B, H, 0, d), np.float16)
+    scale = softmax_scale(d)
+    ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, [hist] * B, rk, rv, [0] * B, scale)
+    pk, pv = oracle.tile_codes(ck, t_cap), oracle.tile_codes(cv, t_cap)
+    out, lse = run_gpu_decode(dims_for(d, dsub, K, H, H), q, cbk, cbv, pk, pv, t_cap, [hist] * B, None, None,
+                              [0] * B, scale)
+    check_attention(out, lse, ref_out, ref_lse)
+    np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-5 * np.abs(ref_out).max())
