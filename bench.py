@@ -363,6 +363,24 @@ def main():
     for c in copies:
         c.clear()
     torch.cuda.synchronize()
+    # context for the roofline: what a plain device copy (torch's copy kernel, 1 GiB read and
+    # 1 GiB written) reaches on this GPU, as (read + write bytes) / time, median of 5
+    if not args.copy_probe:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            dst.copy_(src)
+            c1.record()
+            torch.cuda.synchronize()
+            times.append(c0.elapsed_time(c1))
+        copy_ms = sorted(times)[2]
+        result["roofline"]["copy_gbs"] = round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1)
+        del src, dst
     if args.copy_probe:  # a plain copy of known size, for the byte-counter calibration
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
