@@ -70,24 +70,29 @@ DecodePlan plan_decode(const pqkv_dims& d, int32_t batch, int64_t max_hist_len) 
         p.n_split = 1;
         p.split_tokens = 0;
     } else {
-        // Enough splits to give every compute unit a work-group, then as few splits
-        // (as many rounds per wave, up to cap) as that allows, cut evenly.  A
-        // work-group's fixed costs (codebooks, LUT, epilogue, merge) outweigh a round
-        // of streaming, so longer splits win once every CU is busy.
+        // Every candidate tiles-per-wave count r gives the fewest splits of at most r
+        // rounds, cut evenly, run in the smallest kernel build that holds them.  Its
+        // cost is modelled as the work-group waves the CUs run one after another, each
+        // paying a work-group's fixed costs (codebooks, LUT, epilogue, merge; about 2.4
+        // rounds of streaming), its rounds, and 0.15 round per unused step of the build.
+        // The cheapest wins, fewer work-groups on a tie.
         const int64_t per_tok = kTokensPerRound;
-        int64_t n_split = 0, rounds = 0;
-        auto fit = [&](int cap) {
-            n_split = (kPlanCUs + p.units - 1) / p.units;
-            rounds = (max_hist_len + n_split * per_tok - 1) / (n_split * per_tok);
-            if (rounds < 1) rounds = 1;
-            if (rounds > cap) rounds = cap;
-            n_split = (max_hist_len + rounds * per_tok - 1) / (rounds * per_tok);
-            rounds = (max_hist_len + n_split * per_tok - 1) / (n_split * per_tok);
-        };
-        fit(decode_max_rounds(M, qh));
-        // the 64-subspace kernel runs 9..11 rounds in its 16-round build, whose unused
-        // steps cost more than the extra splits of the 8-round build
-        if (M == 64 && rounds > 8 && rounds < 12) fit(8);
+        int64_t n_split = 0, rounds = 0, best_cost = 0, best_items = 0;
+        for (int r = 1; r <= decode_max_rounds(M, qh); ++r) {
+            const int64_t ns = (max_hist_len + r * per_tok - 1) / (r * per_tok);
+            const int64_t rr = (max_hist_len + ns * per_tok - 1) / (ns * per_tok);
+            // past the merge's split limit only the longest candidate is kept (and refused)
+            if (ns > kMaxSplits && (n_split != 0 || r < decode_max_rounds(M, qh))) continue;
+            const int64_t items = p.units * ns;
+            const int64_t waves = (items + kPlanCUs - 1) / kPlanCUs;
+            const int64_t cost = waves * (48 + 20 * rr + 3 * (decode_kernel_rounds(M, qh, (int)rr) - rr));
+            if (n_split == 0 || cost < best_cost || (cost == best_cost && items < best_items)) {
+                n_split = ns;
+                rounds = rr;
+                best_cost = cost;
+                best_items = items;
+            }
+        }
         p.rounds = (int)rounds;
         p.n_split = (int)n_split;
         p.split_tokens = rounds * kTokensPerRound;

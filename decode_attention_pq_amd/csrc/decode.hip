@@ -28,7 +28,7 @@
 //     address 64 different subspaces and the LDS accesses never conflict; one
 //     v_perm_b32 per code forms the byte address (code << 8) | (4*m), plus
 //     0x10000 for the LUT.
-//   - A wave's tiles per split (RW, 8 or 16) are a template parameter: their
+//   - A wave's tiles per split (RW: 8, 12 or 16) are a template parameter: their
 //     scores stay in registers until the work-group max is known.
 //   - Two-phase softmax inside the work-group: scores stay in registers, the
 //     work-group max is taken once, then p = exp2(s - max) is added into the
@@ -854,8 +854,9 @@ hipError_t launch_qh(const pqkv_dims& d, int32_t batch, const DecodePlan& plan, 
         if (plan.qh == 2) return launch_typed<M, DSUB, 2, decode_max_rounds(M, 2), QT, RT>(d, batch, plan, a, stream);
     }
     if constexpr (M == 64) {
-        if (decode_kernel_rounds(M, 1, plan.rounds) == 8)
-            return launch_typed<M, DSUB, 1, 8, QT, RT>(d, batch, plan, a, stream);
+        const int rw = decode_kernel_rounds(M, 1, plan.rounds);
+        if (rw == 8) return launch_typed<M, DSUB, 1, 8, QT, RT>(d, batch, plan, a, stream);
+        if (rw == 12) return launch_typed<M, DSUB, 1, 12, QT, RT>(d, batch, plan, a, stream);
     }
     return launch_typed<M, DSUB, 1, decode_max_rounds(M, 1), QT, RT>(d, batch, plan, a, stream);
 }

@@ -141,8 +141,11 @@ DECODE_CASES = [
     # enough (sequence, head) units to fill the CUs with one split each: 13 rounds per wave
     # in the 16-round build (three unused steps), ragged and empty rows among them
     (128, 2, 64, 32, 32, (6500, 100, 0, 6144, 6145, 3000, 6600, 5000), (3,) * 8, 8, np.float16),
-    # 10 rounds would be needed: the plan takes two splits of 5 rounds in the 8-round build
+    # 10 rounds per wave in the 12-round build (two unused steps)
     (128, 2, 256, 32, 32, (5000, 4999, 1, 2500, 5000, 4097, 64, 4096), (0, 1, 2, 3, 4, 5, 6, 7), 8, np.float16),
+    # 12 rounds, the 12-round build's full length, and 9 rounds in it
+    (128, 2, 256, 32, 32, (6144, 6100, 0, 12, 6144, 3001, 6143, 64), (2,) * 8, 4, np.float16),
+    (128, 2, 96, 32, 32, (4500, 4400, 4097, 1, 0, 4500, 3000, 4499), (1, 0) * 4, 4, np.float16),
     # d_sub 4, two query heads per work-group, 10 rounds in the 16-round build
     (128, 4, 256, 32, 8, (20000, 19000, 300, 20000), (5, 0, 9, 2), 16, np.float16),
 ]
