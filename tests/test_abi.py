@@ -105,6 +105,30 @@ def test_workspace_formula(P):
     assert L.pqkv_decode_workspace_bytes(_d(P, 128, 4, 256, 32, 8), 1, 131072) == 32 * 16 * 132 * 4 + 256
 
 
+def test_split_plan_choices(P):
+    """The split plan, read back through the workspace size (partials of 132 floats per
+    query head and split, padded to 256 bytes, then one u32 counter per unit, padded)."""
+    L = P.lib()
+    ws = lambda dims, batch, maxh: L.pqkv_decode_workspace_bytes(_d(P, *dims), batch, maxh)
+    pad = lambda n: -(-n // 256) * 256
+    full = (128, 2, 256, 32, 32)
+    # batch 16 x 8192: one 16-round split per (sequence, head), 512 work-groups
+    assert ws(full, 16, 8192) == pad(16 * 32 * 1 * 528) + pad(16 * 32 * 4)
+    # four ragged sequences bounded by 31436 tokens: 4 splits of 8192 per sequence
+    assert ws(full, 4, 31436) == pad(4 * 32 * 4 * 528) + pad(4 * 32 * 4)
+    # batch 16 x 5021: one 10-round split each (12-round build), not two of 5 rounds
+    assert ws(full, 16, 5021) == pad(16 * 32 * 1 * 528) + pad(16 * 32 * 4)
+    # batch 4 x 20083: 4 splits of 10 rounds (512 work-groups), not 3 of 14 (384)
+    assert ws(full, 4, 20083) == pad(4 * 32 * 4 * 528) + pad(4 * 32 * 4)
+    # one head of 300000 tokens: 196 splits of 3 rounds, within the merge's 512-split limit
+    assert ws((128, 2, 256, 1, 1), 1, 300000) == pad(196 * 528) + 256
+    # 5,000,000 tokens need more than 512 splits even at 16 rounds: refused
+    need = ws((128, 2, 256, 1, 1), 1, 5000000)
+    assert need == pad(611 * 528) + 256
+    assert L.pqkv_decode_attention(_d(P, 128, 2, 256, 1, 1), 1, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 5000000, FAKE,
+                                   5000000, FAKE, FAKE, 0, 0, FAKE, 0.088, FAKE, FAKE, FAKE, need, None) == 2
+
+
 def test_merge_validation(P):
     L = P.lib()
     assert L.pqkv_merge(-1, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
