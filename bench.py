@@ -319,10 +319,15 @@ def main():
     enc_flops = enc_pairs * (2 * w.d_sub)
     enc_tflops = enc_flops / (enc_total_ms * 1e-3) / 1e12
     # VALU instructions per pair in the compiled scan (gfx950 asm of encode_kernel).  K a
-    # multiple of 64: d_sub subtractions, d_sub fused multiply-adds, a compare and two selects,
-    # plus a four-instruction merge per block of 64 centroids.  Other K: the same plus an index
-    # move per pair and loop bookkeeping per four pairs.
-    enc_ops_per_pair = 2 * w.d_sub + 3 + 4 / 64 if w.n_centroids % 64 == 0 else 2 * w.d_sub + 4.25
+    # multiple of 64: d_sub subtractions and d_sub fused multiply-adds, half a min (a
+    # three-operand min tree per 16 centroids), a compare and two selects per 16 centroids,
+    # and the rescan of the winning 16 centroids (16 distances, compares and selects plus 4
+    # instructions per subvector).  Other K: the distance, a compare and two selects per
+    # pair, and loop bookkeeping (about 0.3 at d_sub 2, 0.6 at d_sub 4).
+    if w.n_centroids % 64 == 0:
+        enc_ops_per_pair = 2 * w.d_sub + 0.5 + 3 / 16 + (16 * (2 * w.d_sub + 2) + 4) / w.n_centroids
+    else:
+        enc_ops_per_pair = 2 * w.d_sub + 3 + (0.3 if w.d_sub == 2 else 0.6)
     enc_tops = enc_pairs * enc_ops_per_pair / (enc_total_ms * 1e-3) / 1e12
 
     result = {

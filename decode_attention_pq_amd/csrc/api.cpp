@@ -138,7 +138,7 @@ pqkv_status pqkv_encode(const pqkv_dims* dims, const void* x, pqkv_dtype x_dtype
     if (!aligned(x, 16) || x_seq_stride % row_align || x_tok_stride % row_align || x_head_stride % row_align)
         return PQKV_ERR_INVALID;
     if (!aligned(codebook, 16)) return PQKV_ERR_INVALID;
-    if ((n_tokens + 1023) / 1024 > 0x7fffffffLL) return PQKV_ERR_UNSUPPORTED;  // grid x: 1024-token blocks
+    if ((n_tokens + 2047) / 2048 > 0x7fffffffLL) return PQKV_ERR_UNSUPPORTED;  // grid x: blocks of >= 2048 tokens
     return hip_status(launch_encode(*dims, x, x_dtype, n_seqs, n_tokens, x_seq_stride, x_tok_stride,
                                     x_head_stride, codebook, codes, t_cap, t_start, stream));
 }

@@ -6,14 +6,16 @@
 // subvector is the index of the centroid at the smallest squared Euclidean
 // distance, the lowest index winning exact ties.
 //
-// Work decomposition (gfx950): one work-group per (token block, kv head, sequence).
-// The head's codebook (K x d fp32, at most 128 KiB) is staged once into LDS; each
-// lane owns one token and walks its subspaces, holding one subvector (the next
-// one already requested) and scanning all K centroids for it.  All lanes of a
-// wave read the same centroid at the same time, so the LDS reads are broadcasts.
-// The scan is plain fp32 VALU work: (x - c)^2 summed over the subspace, strict '<'
-// in ascending centroid order; with K a multiple of 64 it costs 2*d_sub + 3
-// instructions per (subvector, centroid) pair (nearest_code).
+// Work decomposition (gfx950): one work-group of 1024 threads per (token block,
+// kv head, sequence).  The head's codebook (K x d fp32, at most 128 KiB) is staged
+// once into LDS; each lane owns 4 tokens (d_sub 2) or 2 (d_sub 4) and walks their
+// subspaces, holding one subvector of each (the next ones already requested) and
+// scanning all K centroids for them.  All lanes of a wave read the same centroid
+// at the same time, so the LDS reads are broadcasts, and each value read serves
+// every token of the lane: the LDS traffic per (subvector, centroid) pair is a
+// quarter or a half of one read.  The scan is plain fp32 VALU work: (x - c)^2
+// summed over the subspace, then, for K a multiple of 64, a minimum per 16
+// centroids and a rescan of the winning 16 (nearest_codes).
 
 #include "nearest.h"
 
@@ -21,6 +23,13 @@ namespace pqkv {
 namespace {
 
 constexpr int kEncThreads = 1024;
+// tokens per lane (every centroid value read from LDS serves all of them): as many
+// as the registers of four waves per SIMD hold
+template <int DSUB>
+constexpr int enc_tokens_per_lane() { return DSUB == 2 ? 4 : 2; }
+// floats between sub-blocks of 16 centroid rows in LDS: the sub-blocks that the
+// lanes of a wave rescan start on different banks
+constexpr int kEncPad = 4;
 
 template <int D, int DSUB, typename XT>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(
@@ -28,33 +37,53 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const float* __restrict__ cb, int K, int Hkv, uint8_t* __restrict__ codes, int64_t t_cap,
     int64_t t_start) {
     constexpr int M = D / DSUB;
-    __shared__ float4 cbs4[kLdsRows * D / 4];  // [c][m][j], the global layout
+    // [c][m][j], the global layout, with kEncPad floats after every 16 centroid rows
+    __shared__ float4 cbs4[(kLdsRows * D + kLdsRows / 16 * kEncPad) / 4];
     const float* cbs = reinterpret_cast<const float*>(cbs4);
 
     const int h = blockIdx.y;
     const int b = blockIdx.z;
     const float4* src = reinterpret_cast<const float4*>(cb + (int64_t)h * K * D);
-    for (int i = threadIdx.x; i < K * D / 4; i += kEncThreads) cbs4[i] = src[i];
+    for (int i = threadIdx.x; i < K * D / 4; i += kEncThreads) cbs4[i + i / (4 * D) * (kEncPad / 4)] = src[i];
     __syncthreads();
 
-    const int64_t i = (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
+    // tokens i, i + kEncThreads, ... of the work-group's block
+    constexpr int NT = enc_tokens_per_lane<DSUB>();
+    const int64_t i = (int64_t)blockIdx.x * (NT * kEncThreads) + threadIdx.x;
     if (i >= n_tokens) return;
+    const XT* row[NT];
+    uint8_t* dst[NT];
+    int slot[NT];
+    bool live[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        live[n] = i + n * kEncThreads < n_tokens;
+        const int64_t in = live[n] ? i + n * kEncThreads : i;  // a missing token repeats the first
+        row[n] = x + b * s_seq + in * s_tok + h * s_head;
+        const int64_t t = t_start + in;
+        dst[n] = code_slot<M>(codes + ((int64_t)b * Hkv + h) * t_cap * M, t);
+        slot[n] = (int)(t & (kTileTokens - 1));
+    }
 
-    // One subspace at a time: the next subvector is requested before the current
-    // one is scanned, so its latency hides behind K distance evaluations.
-    const XT* row = x + b * s_seq + i * s_tok + h * s_head;
-    const int64_t t = t_start + i;
-    uint8_t* dst = code_slot<M>(codes + ((int64_t)b * Hkv + h) * t_cap * M, t);
-    const int slot = (int)(t & (kTileTokens - 1));
-    float nxt[DSUB];
-    load_sub<DSUB>(row, nxt);
+    // One subspace at a time: the next subvectors are requested before the current
+    // ones are scanned, so their latency hides behind K distance evaluations.
+    float nxt[NT][DSUB];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) load_sub<DSUB>(row[n], nxt[n]);
 #pragma unroll 1
     for (int m = 0; m < M; ++m) {
-        float xs[DSUB];
+        float xs[NT][DSUB];
 #pragma unroll
-        for (int j = 0; j < DSUB; ++j) xs[j] = nxt[j];
-        load_sub<DSUB>(row + (m + 1 < M ? m + 1 : m) * DSUB, nxt);
-        put_code<M>(dst, slot, m, nearest_code<DSUB, D>(xs, cbs + m * DSUB, K));
+        for (int n = 0; n < NT; ++n) {
+#pragma unroll
+            for (int j = 0; j < DSUB; ++j) xs[n][j] = nxt[n][j];
+            load_sub<DSUB>(row[n] + (m + 1 < M ? m + 1 : m) * DSUB, nxt[n]);
+        }
+        int code[NT];
+        nearest_codes<DSUB, D, kEncPad, NT>(xs, cbs + m * DSUB, K, code);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            if (live[n]) put_code<M>(dst[n], slot[n], m, code[n]);
     }
 }
 
@@ -62,7 +91,8 @@ template <int D, int DSUB, typename XT>
 hipError_t launch_typed(const pqkv_dims& d, const void* x, int32_t n_seqs, int64_t n_tokens,
                         int64_t s_seq, int64_t s_tok, int64_t s_head, const float* cb,
                         uint8_t* codes, int64_t t_cap, int64_t t_start, hipStream_t stream) {
-    dim3 grid((unsigned)((n_tokens + kEncThreads - 1) / kEncThreads), (unsigned)d.n_kv_heads,
+    constexpr int block = enc_tokens_per_lane<DSUB>() * kEncThreads;
+    dim3 grid((unsigned)((n_tokens + block - 1) / block), (unsigned)d.n_kv_heads,
               (unsigned)n_seqs);
     hipLaunchKernelGGL((encode_kernel<D, DSUB, XT>), grid, dim3(kEncThreads), 0, stream,
                        static_cast<const XT*>(x), n_tokens, s_seq, s_tok, s_head, cb,

@@ -55,58 +55,104 @@ __device__ inline float sq_dist(const float (&xs)[DSUB], const C& cc) {
     return dd;
 }
 
-// Index of the centroid nearest to xs among the K centroids at cm, cm + CS, ...
-// (on chip): the smallest squared distance, strict '<' in ascending order, so
-// the lowest index wins exact ties and NaN distances never win.
+// Codes of NT subvectors xs[0..NT) of one subspace: for each, the index of the
+// nearest of the K centroids of an on-chip codebook (centroid c at
+// cm + c*CS + (c/16)*PAD: PAD floats after every 16 rows), i.e. the smallest
+// squared distance, the lowest index among equal ones, NaN distances never
+// winning (a subvector whose distances are all NaN or +inf gets code 0).  Every
+// centroid value read serves all NT subvectors.
 //
-// When K is a multiple of 64 the scan runs in blocks of 64 fully unrolled
-// centroids.  Inside a block the running index is the block-relative position,
-// an inline constant of the select instruction, so a (subvector, centroid) pair
-// costs the distance plus one compare and two selects, with no index register
-// to maintain.  A block's winner replaces the running one only if strictly
-// smaller, which keeps the first minimum overall.
-template <int DSUB, int CS>
-__device__ inline int nearest_code(const float (&xs)[DSUB], const float* cm, int K) {
-    float best = INFINITY;
-    int bi = 0;
+// When K is a multiple of 64 the scan takes two passes over the same fp32
+// distances.  The first keeps only the minimum of every sub-block of 16
+// centroids (three-operand mins, no index bookkeeping) and, across sub-blocks,
+// the first one whose minimum is strictly smaller than all before it.  The
+// second recomputes that sub-block's 16 distances, bit for bit the same
+// instructions, and takes the first one equal to the minimum.  A pair then
+// costs the distance plus half a min in the first pass, and 1/16 of a distance,
+// compare and select in the second, where a single pass needs a compare and two
+// selects per pair.  Lanes read different sub-blocks in the second pass; the
+// PAD floats between sub-blocks put them on different LDS banks.
+template <int DSUB, int CS, int PAD, int NT>
+__device__ inline void nearest_codes(const float (&xs)[NT][DSUB], const float* cm, int K, int (&code)[NT]) {
+    constexpr int SB = 16;  // centroids per sub-block
+    auto row = [&](int c) { return cm + c * CS + (c / SB) * PAD; };
     if ((K & 63) == 0) {
-        // centroid values are read in groups of G (64 floats in registers) before
-        // the group's distances, so the LDS latency is paid once per group
-        constexpr int G = 64 / DSUB;
+        constexpr int G = 64 / DSUB;  // centroids whose values are read together (64 floats)
+        static_assert(G % SB == 0, "a load group holds whole sub-blocks");
+        float best[NT];
+        int bsb[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            best[n] = INFINITY;
+            bsb[n] = 0;
+        }
         for (int c0 = 0; c0 < K; c0 += 64) {
-            const float* cb = cm + c0 * CS;
-            float bb = INFINITY;
-            int br = 0;
+            const float* cb = row(c0);
 #pragma unroll
             for (int g0 = 0; g0 < 64; g0 += G) {
+                // centroid values are read in groups of G before their distances, so
+                // the LDS latency is paid once per group
                 float cv[G][DSUB];
 #pragma unroll
-                for (int r = 0; r < G; ++r) load_sub<DSUB>(cb + (g0 + r) * CS, cv[r]);
+                for (int r = 0; r < G; ++r) load_sub<DSUB>(cb + (g0 + r) * CS + ((g0 + r) / SB) * PAD, cv[r]);
 #pragma unroll
-                for (int r = 0; r < G; ++r) {
-                    const float dd = sq_dist<DSUB>(xs, cv[r]);
-                    if (dd < bb) {
-                        bb = dd;
-                        br = g0 + r;
+                for (int k = 0; k < G / SB; ++k) {
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) {
+                        float d[SB];
+#pragma unroll
+                        for (int r = 0; r < SB; ++r) d[r] = sq_dist<DSUB>(xs[n], cv[k * SB + r]);
+                        const float t0 = fminf(fminf(d[0], d[1]), d[2]);
+                        const float t1 = fminf(fminf(d[3], d[4]), d[5]);
+                        const float t2 = fminf(fminf(d[6], d[7]), d[8]);
+                        const float t3 = fminf(fminf(d[9], d[10]), d[11]);
+                        const float t4 = fminf(fminf(d[12], d[13]), d[14]);
+                        const float u0 = fminf(fminf(t0, t1), t2);
+                        const float u1 = fminf(fminf(t3, t4), d[15]);
+                        const float sm = fminf(u0, u1);
+                        if (sm < best[n]) {
+                            best[n] = sm;
+                            bsb[n] = (c0 + g0) / SB + k;
+                        }
                     }
                 }
             }
-            if (bb < best) {
-                best = bb;
-                bi = c0 + br;
-            }
         }
-    } else {
+        // second pass: the first centroid of sub-block bsb at distance `best`,
+        // scanned downwards so the lowest matching index is the one kept
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const float* sb = row(bsb[n] * SB);
+            int idx = 0;
+#pragma unroll
+            for (int r = SB - 1; r >= 0; --r) {
+                float cv[DSUB];
+                load_sub<DSUB>(sb + r * CS, cv);
+                idx = sq_dist<DSUB>(xs[n], cv) == best[n] ? r : idx;
+            }
+            code[n] = bsb[n] * SB + idx;
+        }
+        return;
+    }
+    float best[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        best[n] = INFINITY;
+        code[n] = 0;
+    }
 #pragma unroll 4
-        for (int c = 0; c < K; ++c) {
-            const float dd = sq_dist<DSUB>(xs, cm + c * CS);
-            if (dd < best) {
-                best = dd;
-                bi = c;
+    for (int c = 0; c < K; ++c) {
+        float cv[DSUB];
+        load_sub<DSUB>(row(c), cv);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const float dd = sq_dist<DSUB>(xs[n], cv);
+            if (dd < best[n]) {
+                best[n] = dd;
+                code[n] = c;
             }
         }
     }
-    return bi;
 }
 
 // Byte m of a token's code goes to the rotated position of its slot in the tile
@@ -125,10 +171,12 @@ __device__ inline void write_nearest_codes_slice(const float (&xv)[MW * DSUB], c
                                                  uint8_t* dst, int slot, int m0) {
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi) {
-        float xs[DSUB];
+        float xs[1][DSUB];
 #pragma unroll
-        for (int j = 0; j < DSUB; ++j) xs[j] = xv[mi * DSUB + j];
-        put_code<D / DSUB>(dst, slot, m0 + mi, nearest_code<DSUB, CS>(xs, cbs + mi * DSUB, K));
+        for (int j = 0; j < DSUB; ++j) xs[0][j] = xv[mi * DSUB + j];
+        int code[1];
+        nearest_codes<DSUB, CS, 0, 1>(xs, cbs + mi * DSUB, K, code);
+        put_code<D / DSUB>(dst, slot, m0 + mi, code[0]);
     }
 }
 

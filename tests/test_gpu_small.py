@@ -53,9 +53,11 @@ def test_encode_matches_oracle(d, dsub, K, dtype):
 
 
 @pytest.mark.parametrize("K,keep,dups", [(64, 7, (40, 63)), (256, 70, (130, 200, 255)), (256, 7, (64, 100)),
-                                         (48, 5, (17, 47))])
+                                         (48, 5, (17, 47)), (128, 3, (5, 15)), (256, 17, (18, 31, 32, 47)),
+                                         (256, 240, (241, 255))])
 def test_encode_duplicate_centroids_lowest_index(K, keep, dups):
-    # exact ties, inside one block of 64 centroids and across blocks: the lowest index wins
+    # exact ties inside one sub-block of 16 centroids, across sub-blocks and across
+    # blocks of 64: the lowest index wins
     d, dsub, H = 128, 2, 2
     M = d // dsub
     cb = _codebook(5, H, K, M, dsub)
