@@ -52,6 +52,26 @@ def test_encode_matches_oracle(d, dsub, K, dtype):
         check_codes(got, x[s], cb, ref, d1, d2)
 
 
+@pytest.mark.parametrize("d,dsub", [(128, 2), (128, 4), (64, 2), (64, 4)])
+@pytest.mark.parametrize("K", [64, 192])
+def test_encode_several_tokens_per_lane(d, dsub, K):
+    # 2500 tokens: every lane scans 2 or 4 tokens (one to three of them live in the
+    # last block), over 1 or 3 blocks of 64 centroids
+    H, N, t_cap, t_start = 2, 2500, 2560, 40
+    M = d // dsub
+    x = _outlier_values(d * 3 + K + dsub, (1, N, H, d), np.float16)
+    cb = _codebook(K * 5 + dsub, H, K, M, dsub)
+    fill = np.full((1, H, t_cap * M), 0xAB, np.uint8)
+    planes = run_gpu_encode(dims_for(d, dsub, K, H, H), x, cb, 1, t_cap, t_start, init_codes=fill)
+    off = oracle.code_offsets(M, t_cap)
+    written = np.zeros(t_cap * M, bool)
+    written[off[t_start:t_start + N].ravel()] = True
+    assert np.all(planes[..., ~written] == 0xAB), "bytes outside the encoded tokens changed"
+    ref, d1, d2, amb = oracle.encode(x[0], cb)
+    got = oracle.untile_codes(planes[0], t_start + N, M)[:, t_start:].transpose(1, 0, 2)
+    check_codes(got, x[0], cb, ref, d1, d2)
+
+
 @pytest.mark.parametrize("K,keep,dups", [(64, 7, (40, 63)), (256, 70, (130, 200, 255)), (256, 7, (64, 100)),
                                          (48, 5, (17, 47)), (128, 3, (5, 15)), (256, 17, (18, 31, 32, 47)),
                                          (256, 240, (241, 255))])
