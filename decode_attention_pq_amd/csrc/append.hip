@@ -65,7 +65,8 @@ __global__ __launch_bounds__(kAppThreads) void roll_kernel(AppendArgs a) {
     constexpr int MW = SW / kAppWaves;       // subspaces per wave
     constexpr int CS = SW * DSUB;            // floats per staged centroid row
     static_assert(M % SW == 0 && SW % kAppWaves == 0, "roll subspace split");
-    __shared__ float cbs[kLdsRows * CS];
+    constexpr int PAD = 4;                   // floats after every 16 centroid rows (bank spread)
+    __shared__ __align__(16) float cbs[kLdsRows * CS + kLdsRows / 16 * PAD];
     const int g = blockIdx.x % (M / SW);     // subspace group
     const int rb = blockIdx.x / (M / SW);    // block of 64 rolled rows
     const int h = blockIdx.y;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(kAppThreads) void roll_kernel(AppendArgs a) {
 
     // stage subspaces [g*SW, g*SW + SW) of every centroid: CS contiguous floats per row
     const float* cb = (tensor ? a.cb_v : a.cb_k) + (int64_t)h * a.K * D + g * CS;
-    for (int i = tid; i < a.K * CS; i += kAppThreads) cbs[i] = cb[(i / CS) * D + i % CS];
+    for (int i = tid; i < a.K * CS; i += kAppThreads) cbs[i + i / (16 * CS) * PAD] = cb[(i / CS) * D + i % CS];
     __syncthreads();
     const int row = rb * 64 + lane;
     if (row < a.n_roll) {
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(kAppThreads) void roll_kernel(AppendArgs a) {
         for (int j = 0; j < MW * DSUB; ++j) xv[j] = to_float(rows[(int64_t)row * D + m0 * DSUB + j]);
         uint8_t* plane = (tensor ? a.codes_v : a.codes_k) + ((int64_t)b * a.Hkv + h) * a.t_cap * M;
         const int64_t t = T + row;
-        write_nearest_codes_slice<D, DSUB, MW, CS>(xv, cbs + wave * MW * DSUB, a.K, code_slot<M>(plane, t),
+        write_nearest_codes_slice<D, DSUB, MW, CS, PAD>(xv, cbs + wave * MW * DSUB, a.K, code_slot<M>(plane, t),
                                                    (int)(t & (kTileTokens - 1)), m0);
     }
 }

@@ -165,8 +165,9 @@ __device__ inline void put_code(uint8_t* dst, int slot, int m, int code) {
 
 // Codes of subspaces m0 .. m0 + MW - 1 of one token.  xv holds those subspaces'
 // values (MW * DSUB floats, subspace m0 first); `cbs` points at subspace m0 of
-// centroid 0 of an on-chip codebook whose centroid rows are CS floats apart.
-template <int D, int DSUB, int MW, int CS>
+// centroid 0 of an on-chip codebook whose centroid rows are CS floats apart, with
+// PAD floats after every 16 rows.
+template <int D, int DSUB, int MW, int CS, int PAD>
 __device__ inline void write_nearest_codes_slice(const float (&xv)[MW * DSUB], const float* cbs, int K,
                                                  uint8_t* dst, int slot, int m0) {
 #pragma unroll
@@ -175,7 +176,7 @@ __device__ inline void write_nearest_codes_slice(const float (&xv)[MW * DSUB], c
 #pragma unroll
         for (int j = 0; j < DSUB; ++j) xs[0][j] = xv[mi * DSUB + j];
         int code[1];
-        nearest_codes<DSUB, CS, 0, 1>(xs, cbs + mi * DSUB, K, code);
+        nearest_codes<DSUB, CS, PAD, 1>(xs, cbs + mi * DSUB, K, code);
         put_code<D / DSUB>(dst, slot, m0 + mi, code[0]);
     }
 }
