@@ -130,7 +130,9 @@ __device__ inline void nearest_codes(const float (&xs)[NT][DSUB], const float* c
                 load_sub<DSUB>(sb + r * CS, cv);
                 idx = sq_dist<DSUB>(xs[n], cv) == best[n] ? r : idx;
             }
-            code[n] = bsb[n] * SB + idx;
+            // no distance below +inf: code 0, as the plain scan gives (this also holds
+            // when a non-finite codebook mixes +inf and NaN distances)
+            code[n] = best[n] < INFINITY ? bsb[n] * SB + idx : 0;
         }
         return;
     }
