@@ -95,7 +95,7 @@ def test_workspace_formula(P):
     L = P.lib()
     # partials (132 floats per query head and split) padded to 256 bytes, then one
     # u32 completion counter per (sequence, kv head, query-head group), padded
-    # config-2 shape: 32 kv heads, one query head each, 8 splits of 4096 tokens
+    # LLaMA-2-7B shape at 32K context: 32 kv heads, one query head each, 8 splits of 4096 tokens
     assert L.pqkv_decode_workspace_bytes(_d(P, 128, 2, 256, 32, 32), 1, 32768) == 32 * 8 * 132 * 4 + 256
     # no history: one split per unit for the recent window
     assert L.pqkv_decode_workspace_bytes(_d(P, 128, 2, 256, 32, 32), 1, 0) == 32 * 1 * 132 * 4 + 256
