@@ -403,8 +403,8 @@ def main():
 
 def cpu_baseline(w, target_s, check=None):
     """The CPU oracle (fp64 dequantise-then-exact attention) on a sample of the same workload:
-    the first kv heads (and their query heads) of sequence 0, scaled to the whole call by the
-    head count.  With `check` (copy 0's inputs and the GPU's output for them) the sample is
+    the first kv heads (and their query heads, at least one per host thread) of sequence 0,
+    scaled to the whole call by the head count; then the same on one thread and one kv head.  With `check` (copy 0's inputs and the GPU's output for them) the sample is
     that copy's real codes and the oracle's result is compared with the GPU's, at the
     attention tolerance (2e-3, row-normwise); otherwise seeded random codes stand in."""
     import oracle
@@ -413,7 +413,9 @@ def cpu_baseline(w, target_s, check=None):
     d, M, K = w.head_dim, w.n_sub, w.n_centroids
     g = w.n_q_heads // w.n_kv_heads
     R = w.recent_len
-    hk = min(4, w.n_kv_heads)
+    # the oracle runs one thread per query head: sample enough heads for every host thread
+    threads = oracle.max_threads()
+    hk = min(w.n_kv_heads, max(4, -(-threads // g)))
     hq = hk * g
     scale = float(np.float32(1.0 / math.sqrt(d)))
     if check is not None:
@@ -441,11 +443,28 @@ def cpu_baseline(w, target_s, check=None):
             break
     el = time.time() - t0
     per_call = el / reps * (w.n_q_heads / hq)
-    baseline = {"value": round((T + R) / per_call, 1), "unit": "KV tokens/s", "cores": oracle.max_threads(),
+    cores = min(threads, hq)
+    baseline = {"value": round((T + R) / per_call, 1), "unit": "KV tokens/s", "cores": cores,
                 "kind": "oracle",
                 "sample": f"{reps} x fp64 dequantise-then-exact attention over {hq} of {w.n_q_heads} query heads "
                           f"of sequence 0 ({T}+{R} tokens, {'copy 0 of the timed inputs' if check else 'random codes'}),"
                           f" scaled to all heads; {el:.1f}s"}
+    # the same oracle on one thread, one kv head's query heads, for about a third of the time
+    oracle.set_threads(1)
+    try:
+        t1, reps1 = time.time(), 0
+        while True:
+            oracle.decode_exact(q[:, :g], cbk[:1], cbv[:1], ck[:, :1], cv[:, :1], [T], rk[:, :1], rv[:, :1], [R], scale)
+            reps1 += 1
+            if time.time() - t1 >= target_s / 3:
+                break
+        el1 = time.time() - t1
+    finally:
+        oracle.set_threads(threads)
+    per_call1 = el1 / reps1 * (w.n_q_heads / g)
+    baseline["one_thread"] = {"value": round((T + R) / per_call1, 1), "cores": 1,
+                              "sample": f"{reps1} x the same over {g} of {w.n_q_heads} query heads, "
+                                        f"scaled to all heads; {el1:.1f}s"}
     parity = None
     if check is not None:
         got, got_lse = check["out"][0, :hq].astype(np.float64), check["lse"][0, :hq].astype(np.float64)
