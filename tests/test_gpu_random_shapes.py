@@ -1,23 +1,26 @@
-"""Seeded sweep of random decode shapes against the oracle.
+"""Seeded sweeps of random decode and encode shapes against the oracle.
 
-Twenty-four shapes drawn from one seed cover the combinations the hand-written
-cases do not list: head size, subspace size, centroid count (2..256), kv and
+Ninety-six decode shapes drawn from one seed cover the combinations the
+hand-written cases do not list: head size, subspace size, centroid count (2..256), kv and
 query heads (groups of 1, 2, 4 and 8), batch 1..5 with independent history
 lengths (empty, sub-tile, multi-split), recent windows from none to 300 rows,
 fp16 and fp32.  Every case runs the HIP decode through the C ABI and compares
-it with the dequantise-then-exact oracle at the usual tolerance.
+it with the dequantise-then-exact oracle at the usual tolerance.  Forty-eight
+encode shapes (head size, subspace size, centroid counts with and without whole
+blocks of 64, 1..3 heads, 1..4999 tokens at a random start, one or two
+sequences, fp16 and fp32, outlier-heavy values) are compared code by code.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synthkv
-from pqkv_testlib import check_attention, dims_for, run_gpu_decode, softmax_scale
+from pqkv_testlib import check_attention, check_codes, dims_for, run_gpu_decode, run_gpu_encode, softmax_scale
 
 pytestmark = pytest.mark.gpu
 
 
-def _shapes(n=24, seed=2024):
+def _shapes(n=96, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(n):
@@ -57,3 +60,37 @@ def test_random_shape_decode(case):
                               hist, np.ascontiguousarray(rk) if r_cap else None,
                               np.ascontiguousarray(rv) if r_cap else None, rec, scale)
     check_attention(out, lse, ref_out, ref_lse)
+
+
+def _encode_shapes(n=48, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        dsub = int(rng.choice([2, 4]))
+        K = int(rng.choice([16, 37, 64, 128, 192, 200, 256]))
+        H = int(rng.integers(1, 4))
+        N = int(rng.integers(1, 5000))
+        ns = int(rng.integers(1, 3))
+        t_start = int(rng.integers(0, 100))
+        dt = np.float16 if rng.random() < 0.6 else np.float32
+        out.append((d, dsub, K, H, N, ns, t_start, dt, 3000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _encode_shapes(), ids=lambda c: f"d{c[0]}s{c[1]}K{c[2]}h{c[3]}n{c[4]}x{c[5]}")
+def test_random_shape_encode(case):
+    d, dsub, K, H, N, ns, t_start, dt, seed = case
+    M = d // dsub
+    t_cap = -(-(t_start + N) // 64) * 64
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((ns, N, H, d)).astype(np.float32)
+    x[..., :3] *= 10.0
+    x[rng.random(x.shape) < 0.01] *= 20.0
+    x = x.astype(dt)
+    cb = (np.random.default_rng(seed + 1).standard_normal((H, K, M, dsub)) * 3).astype(np.float32)
+    planes = run_gpu_encode(dims_for(d, dsub, K, H, H), x, cb, ns, t_cap, t_start)
+    for s in range(ns):
+        ref, d1, d2, _ = oracle.encode(x[s], cb)
+        got = oracle.untile_codes(planes[s], t_start + N, M)[:, t_start:].transpose(1, 0, 2)
+        check_codes(got, x[s], cb, ref, d1, d2)
