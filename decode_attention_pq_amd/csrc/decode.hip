@@ -28,7 +28,7 @@
 //     address 64 different subspaces and the LDS accesses never conflict; one
 //     v_perm_b32 per code forms the byte address (code << 8) | (4*m), plus
 //     0x10000 for the LUT.
-//   - A wave's tiles per split (RW: 8, 12 or 16) are a template parameter: their
+//   - A wave's tiles per split (RW: 2 to 16) are a template parameter: their
 //     scores stay in registers until the work-group max is known.
 //   - Two-phase softmax inside the work-group: scores stay in registers, the
 //     work-group max is taken once, then p = exp2(s - max) is added into the
@@ -855,6 +855,8 @@ hipError_t launch_qh(const pqkv_dims& d, int32_t batch, const DecodePlan& plan, 
     }
     if constexpr (M == 64) {
         const int rw = decode_kernel_rounds(M, 1, plan.rounds);
+        if (rw == 2) return launch_typed<M, DSUB, 1, 2, QT, RT>(d, batch, plan, a, stream);
+        if (rw == 4) return launch_typed<M, DSUB, 1, 4, QT, RT>(d, batch, plan, a, stream);
         if (rw == 8) return launch_typed<M, DSUB, 1, 8, QT, RT>(d, batch, plan, a, stream);
         if (rw == 12) return launch_typed<M, DSUB, 1, 12, QT, RT>(d, batch, plan, a, stream);
     }
