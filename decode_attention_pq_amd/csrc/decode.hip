@@ -844,23 +844,30 @@ hipError_t launch_typed(const pqkv_dims& d, int32_t batch, const DecodePlan& pla
     return hipGetLastError();
 }
 
+// The build that holds the plan's rounds (decode_kernel_rounds).
+template <int M, int DSUB, int QH, typename QT, typename RT>
+hipError_t launch_rw(const pqkv_dims& d, int32_t batch, const DecodePlan& plan, const DecodeArgs& a,
+                     hipStream_t stream) {
+    const int rw = decode_kernel_rounds(M, QH, plan.rounds);
+    if constexpr (M == 64) {
+        if (rw == 2) return launch_typed<M, DSUB, QH, 2, QT, RT>(d, batch, plan, a, stream);
+        if (rw == 8) return launch_typed<M, DSUB, QH, 8, QT, RT>(d, batch, plan, a, stream);
+        if (rw == 12) return launch_typed<M, DSUB, QH, 12, QT, RT>(d, batch, plan, a, stream);
+    }
+    if (rw == 4) return launch_typed<M, DSUB, QH, 4, QT, RT>(d, batch, plan, a, stream);
+    return launch_typed<M, DSUB, QH, decode_max_rounds(M, QH), QT, RT>(d, batch, plan, a, stream);
+}
+
 template <int M, int DSUB, typename QT, typename RT>
 hipError_t launch_qh(const pqkv_dims& d, int32_t batch, const DecodePlan& plan, const DecodeArgs& a,
                      hipStream_t stream) {
     if constexpr (M <= 16) {
-        if (plan.qh == 4) return launch_typed<M, DSUB, 4, decode_max_rounds(M, 4), QT, RT>(d, batch, plan, a, stream);
+        if (plan.qh == 4) return launch_rw<M, DSUB, 4, QT, RT>(d, batch, plan, a, stream);
     }
     if constexpr (M <= 32) {
-        if (plan.qh == 2) return launch_typed<M, DSUB, 2, decode_max_rounds(M, 2), QT, RT>(d, batch, plan, a, stream);
+        if (plan.qh == 2) return launch_rw<M, DSUB, 2, QT, RT>(d, batch, plan, a, stream);
     }
-    if constexpr (M == 64) {
-        const int rw = decode_kernel_rounds(M, 1, plan.rounds);
-        if (rw == 2) return launch_typed<M, DSUB, 1, 2, QT, RT>(d, batch, plan, a, stream);
-        if (rw == 4) return launch_typed<M, DSUB, 1, 4, QT, RT>(d, batch, plan, a, stream);
-        if (rw == 8) return launch_typed<M, DSUB, 1, 8, QT, RT>(d, batch, plan, a, stream);
-        if (rw == 12) return launch_typed<M, DSUB, 1, 12, QT, RT>(d, batch, plan, a, stream);
-    }
-    return launch_typed<M, DSUB, 1, decode_max_rounds(M, 1), QT, RT>(d, batch, plan, a, stream);
+    return launch_rw<M, DSUB, 1, QT, RT>(d, batch, plan, a, stream);
 }
 
 template <typename QT, typename RT>

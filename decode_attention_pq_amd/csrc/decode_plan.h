@@ -24,10 +24,10 @@ constexpr int decode_max_rounds(int n_sub, int qh) { return qh == 4 ? 8 : 16; }
 // Tiles per wave of the kernel build that runs a split of `rounds` tiles per wave:
 // the smallest build that holds them.  Steps past the plan's rounds still issue
 // their (dummy) loads, so the 64-subspace kernel comes in 2-, 4-, 8-, 12- and
-// 16-round builds.
+// 16-round builds, and the narrower ones in a 4-round build beside the longest.
 constexpr int decode_kernel_rounds(int n_sub, int qh, int rounds) {
     return n_sub == 64 ? (rounds <= 2 ? 2 : rounds <= 4 ? 4 : rounds <= 8 ? 8 : rounds <= 12 ? 12 : 16)
-                       : decode_max_rounds(n_sub, qh);
+                       : (rounds <= 4 ? 4 : decode_max_rounds(n_sub, qh));
 }
 // Splits per unit the merge can take (its split maxima and sums live in LDS).
 constexpr int kMaxSplits = 512;
