@@ -165,6 +165,8 @@ DECODE_CASES = [
     (128, 2, 64, 32, 32, (6500, 100, 0, 6144, 6145, 3000, 6600, 5000), (3,) * 8, 8, np.float16),
     # 10 rounds per wave in the 12-round build (two unused steps)
     (128, 2, 256, 32, 32, (5000, 4999, 1, 2500, 5000, 4097, 64, 4096), (0, 1, 2, 3, 4, 5, 6, 7), 8, np.float16),
+    # 2 rounds, the 2-round build's full length, ragged, with empty rows
+    (128, 2, 256, 32, 32, (1000, 513, 0, 1024, 999, 64, 1, 700), (2, 0) * 4, 4, np.float16),
     # 4 rounds (the 4-round build) and 3 rounds in it, ragged, with empty rows
     (128, 2, 256, 32, 32, (2000, 1900, 0, 1, 2048, 1500, 64, 1999), (4, 0) * 4, 4, np.float16),
     (128, 2, 256, 32, 32, (1536, 1000, 1535, 0, 1200, 1, 513, 1536), (0, 3) * 4, 4, np.float16),
