@@ -40,7 +40,8 @@
 //   - Each work-group also takes a slice of the recent window (exact fp32 dot
 //     products), writes its partial (max, sum, unnormalised output), and the
 //     last work-group of a (sequence, kv head, group) to finish merges all
-//     partials into out and lse (completion counter in the workspace).
+//     partials into out and lse (completion counter in the workspace).  A unit
+//     whose history fits one split writes out and lse directly.
 
 #include <hip/hip_fp16.h>
 
@@ -251,6 +252,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     __shared__ float redl[kWaves * QH];  // per-wave bounds on the history weight sums
     __shared__ float redr[kWaves * QH];  // per-wave recent weight sums
     __shared__ uint32_t redu[kWaves * QH];
+    __shared__ float lfin[QH];           // single-split units: the weight sums
     __shared__ int last_flag;
     uint32_t* hist = reinterpret_cast<uint32_t*>(lds);
     float* table = lds + kLdsRows * kRow;
@@ -716,6 +718,39 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
             for (int i = 0; i < CPL; ++i) ored[(wave * QH + j) * D + em * DSUB + ecomp + i] = acc[j][i];
     }
     __syncthreads();
+    if (ns == 1) {
+        // The unit's only split: it normalises its own output, with no partial
+        // round trip.  The result is the one the merge gives for a single split
+        // (the fixed-point scale cancels exactly, being a power of two).
+        if (tid < QH) {
+            uint32_t lh = 0u;
+            float lr = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                lh += redu[w * QH + tid];
+                lr += redr[w * QH + tid];
+            }
+            lfin[tid] = (float)lh + lr;
+        }
+        __syncthreads();
+        for (int e = tid; e < QH * D; e += kThreads) {
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) s += ored[w * QH * D + e];
+            const int j = e / D;
+            const int el = e - j * D;
+            float m = mx[0], inv = fi[0];
+#pragma unroll
+            for (int q = 1; q < QH; ++q) {
+                m = j == q ? mx[q] : m;
+                inv = j == q ? fi[q] : inv;
+            }
+            const int64_t orow = (int64_t)(b * a.Hq + hq0 + j);
+            a.out[orow * D + el] = any ? (s * inv) / (lfin[j] * inv) : 0.0f;
+            if (el == 0) a.lse[orow] = any ? (m + log2f(lfin[j] * inv)) * kLn2 : -INFINITY;
+        }
+        return;
+    }
     // Partials are published with agent-scope stores, which write through the
     // XCD-private L2, so the merging work-group on another XCD reads them from memory.
     for (int e = tid; e < QH * D; e += kThreads) {
