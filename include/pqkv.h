@@ -158,6 +158,9 @@ size_t pqkv_decode_workspace_bytes(const pqkv_dims* dims, int32_t batch, int64_t
  *                 it (e.g. one hipMemset); every call leaves it ready for the next one.  It
  *                 holds per-split partial results and per-(sequence, kv head) completion
  *                 counters, so calls sharing one workspace must be ordered on one stream.
+ * The call allocates nothing, records no memset and never waits on the host, so
+ * it may be captured in a HIP graph and replayed with new device-side q and
+ * lengths (max_hist_len, fixed at capture, must still bound them).
  * Device-side lengths outside their bounds are clamped to them.  Errors: INVALID
  * for null pointers, negative sizes, max_hist_len > t_cap, bad dtype;
  * UNSUPPORTED for dims outside the ranges above or r_cap > PQKV_MAX_RECENT;
