@@ -336,3 +336,26 @@ def test_decode_identical_tokens_fill_one_cell(B, H, hist):
                               [0] * B, scale)
     check_attention(out, lse, ref_out, ref_lse)
     np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-5 * np.abs(ref_out).max())
+
+
+@pytest.mark.parametrize("dsub", [2, 4])
+def test_decode_large_magnitudes(dsub):
+    """Queries 40x and codebooks 30x the unit scale (outlier-sized values, scores in the
+    thousands): the softmax is sharply peaked and fp32 LUT sums carry large terms."""
+    d, K, Hq, Hkv, r_cap = 128, 256, 8, 4, 32
+    hist, rec = (3000, 9000), (32, 5)
+    B, M = len(hist), d // dsub
+    t_cap = -(-max(hist) // 64) * 64
+    seed = 4040 + dsub
+    q = (synthkv.small_normal(seed, (B, Hq, d)) * 40).astype(np.float16)
+    cbk = _codebook(seed + 1, Hkv, K, M, dsub, 30.0)
+    cbv = _codebook(seed + 2, Hkv, K, M, dsub, 30.0)
+    ck = synthkv.small_codes(seed + 3, (B, Hkv, t_cap, M), K)
+    cv = synthkv.small_codes(seed + 4, (B, Hkv, t_cap, M), K)
+    rk = (synthkv.small_normal(seed + 5, (B, Hkv, r_cap, d)) * 40).astype(np.float16)
+    rv = (synthkv.small_normal(seed + 6, (B, Hkv, r_cap, d)) * 40).astype(np.float16)
+    scale = softmax_scale(d)
+    ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, hist, rk, rv, rec, scale)
+    out, lse = run_gpu_decode(dims_for(d, dsub, K, Hq, Hkv), q, cbk, cbv, oracle.tile_codes(ck, t_cap),
+                              oracle.tile_codes(cv, t_cap), t_cap, hist, rk, rv, rec, scale)
+    check_attention(out, lse, ref_out, ref_lse)
