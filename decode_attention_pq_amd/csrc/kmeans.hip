@@ -16,7 +16,10 @@
 //   3. `iters` Lloyd iterations: every point takes its nearest centroid (squared
 //      distance, strict '<' in ascending centroid order, so the lowest index wins
 //      ties), then thread c moves centroid c to the mean of its members, summing
-//      them in point order; an empty cluster keeps its centroid.
+//      them in point order; an empty cluster keeps its centroid.  While assigning,
+//      each point also sets its 32-point block's bit in its centroid's block mask,
+//      so thread c scans only the blocks that hold members of c (in ascending
+//      order, which keeps the point order of the sums).
 // Arithmetic is fp64 with every product and sum rounded on its own (no fused
 // multiply-add), so distances, sums and means are the IEEE results of the plain
 // definition, whatever the thread count.
@@ -29,6 +32,8 @@ namespace pqkv {
 namespace {
 
 constexpr int kKmThreads = 256;
+constexpr int kBlkPts = 32;                                   // points per mask bit
+constexpr int kMaskWords = (PQKV_MAX_FIT_POINTS + kBlkPts * 32 - 1) / (kBlkPts * 32);  // per centroid
 
 template <typename XT>
 __device__ inline float elem(const XT* p) {
@@ -113,6 +118,7 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_kernel(KmArgs a) {
     extern __shared__ float dyn[];
     __shared__ double C[kLdsRows * DSUB];
     __shared__ int kept_s;
+    __shared__ uint32_t bmask[kLdsRows * kMaskWords];  // centroid c's blocks: bmask[c * kMaskWords ...]
     const int m = blockIdx.x;
     const int h = blockIdx.y;
     const int tid = threadIdx.x;
@@ -161,12 +167,17 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_kernel(KmArgs a) {
     __syncthreads();
 
     // ---- Lloyd iterations
+    const int mask_words = (int)((n + kBlkPts * 32 - 1) / (kBlkPts * 32));
+    for (int i = tid; i < K * kMaskWords; i += kKmThreads) bmask[i] = 0u;
+    __syncthreads();
     for (int it = 0; it < a.iters; ++it) {
         for (int64_t i = tid; i < n; i += kKmThreads) {
             double xd[DSUB];
 #pragma unroll
             for (int j = 0; j < DSUB; ++j) xd[j] = (double)pts[i * DSUB + j];
-            asg[i] = (uint8_t)nearest_centroid<DSUB>(xd, C, K);
+            const int c = nearest_centroid<DSUB>(xd, C, K);
+            asg[i] = (uint8_t)c;
+            atomicOr(&bmask[c * kMaskWords + (int)(i / (kBlkPts * 32))], 1u << ((i / kBlkPts) & 31));
         }
         __syncthreads();
         // the update reads only assignments and points, so centroid c can be
@@ -176,11 +187,35 @@ __global__ __launch_bounds__(kKmThreads) void kmeans_kernel(KmArgs a) {
 #pragma unroll
             for (int j = 0; j < DSUB; ++j) sum[j] = 0.0;
             int64_t cnt = 0;
-            for (int64_t i = 0; i < n; ++i) {
-                if (asg[i] == tid) {
-                    ++cnt;
+            auto add = [&](int64_t i) {
+                ++cnt;
 #pragma unroll
-                    for (int j = 0; j < DSUB; ++j) sum[j] = __dadd_rn(sum[j], (double)pts[i * DSUB + j]);
+                for (int j = 0; j < DSUB; ++j) sum[j] = __dadd_rn(sum[j], (double)pts[i * DSUB + j]);
+            };
+            // within a block, the assignments four at a time: a word that holds no
+            // byte equal to this centroid costs a few integer operations; a word that
+            // may hold one is checked byte by byte, in point order
+            const uint32_t pat = (uint32_t)tid * 0x01010101u;
+            const uint32_t* a4 = reinterpret_cast<const uint32_t*>(asg);
+            for (int w = 0; w < mask_words; ++w) {
+                uint32_t bits = bmask[tid * kMaskWords + w];
+                bmask[tid * kMaskWords + w] = 0u;  // cleared for the next iteration
+                while (bits) {
+                    const int64_t i0 = ((int64_t)w * 32 + __builtin_ctz(bits)) * kBlkPts;
+                    bits &= bits - 1;
+                    const int64_t i1 = i0 + kBlkPts < n ? i0 + kBlkPts : n;
+                    int64_t i = i0;
+                    for (; i + 4 <= i1; i += 4) {
+                        const uint32_t wv = a4[i / 4];
+                        const uint32_t mz = wv ^ pat;
+                        if ((mz - 0x01010101u) & ~mz & 0x80808080u) {  // some byte of mz is zero
+#pragma unroll
+                            for (int k = 0; k < 4; ++k)
+                                if (((wv >> (8 * k)) & 0xffu) == (uint32_t)tid) add(i + k);
+                        }
+                    }
+                    for (; i < i1; ++i)
+                        if (asg[i] == tid) add(i);
                 }
             }
             if (cnt > 0)

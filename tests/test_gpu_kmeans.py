@@ -84,3 +84,19 @@ def test_fit_strided_fp32_input():
     order = np.stack([np.stack([np.random.default_rng(66 + 32 * h + m).permutation(700) for m in range(32)])
                       for h in range(3)])
     _check(values.astype(np.float32), 2, 100, 7, order, head_stride_pad=32)
+
+
+def test_fit_ragged_point_count():
+    # neither a multiple of 4 (the word-wise assignment scan) nor of 32 (one bit of a
+    # centroid's block mask)
+    values = synthkv.small_normal(67, (203, 2, 64)).astype(np.float16)
+    order = np.stack([np.stack([np.random.default_rng(68 + 32 * h + m).permutation(203) for m in range(32)])
+                      for h in range(2)])
+    _check(values, 2, 64, 4, order)
+
+
+def test_fit_maximum_point_count():
+    n = 8192  # the largest fit, whose points, assignments and masks fill most of LDS
+    values = synthkv.small_normal(69, (n, 1, 128)).astype(np.float16)
+    order = np.stack([np.stack([np.random.default_rng(70 + m).permutation(n) for m in range(32)])])
+    _check(values, 4, 256, 2, order)
