@@ -86,13 +86,15 @@ def test_fit_strided_fp32_input():
     _check(values.astype(np.float32), 2, 100, 7, order, head_stride_pad=32)
 
 
-def test_fit_ragged_point_count():
+@pytest.mark.parametrize("d_sub,K", [(2, 64), (4, 100)])
+def test_fit_ragged_point_count(d_sub, K):
     # neither a multiple of 4 (the word-wise assignment scan) nor of 32 (one bit of a
-    # centroid's block mask)
+    # centroid's block mask); K 100 takes the plain (not 16-blocked) nearest-centroid scan
     values = synthkv.small_normal(67, (203, 2, 64)).astype(np.float16)
-    order = np.stack([np.stack([np.random.default_rng(68 + 32 * h + m).permutation(203) for m in range(32)])
+    M = 64 // d_sub
+    order = np.stack([np.stack([np.random.default_rng(68 + 32 * h + m).permutation(203) for m in range(M)])
                       for h in range(2)])
-    _check(values, 2, 64, 4, order)
+    _check(values, d_sub, K, 4, order)
 
 
 def test_fit_maximum_point_count():
