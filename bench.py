@@ -52,7 +52,8 @@ def parse():
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 COUNTERS = os.path.join(ROOT, "profiles", "pq_decode_kernel__llama2_7b_32k.counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_pq_amd", "csrc", f) for f in ("decode.hip", "decode_plan.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_pq_amd", "csrc", f)
+                  for f in ("decode_kernel.h", "decode_m64d2.hip", "decode_plan.h")]
 
 
 def kernel_source_hash() -> str:

@@ -65,8 +65,8 @@ def lib() -> ctypes.CDLL:
         L.pqkv_build_lut.restype = i32
         L.pqkv_decode_workspace_bytes.argtypes = [dp, i32, i64]
         L.pqkv_decode_workspace_bytes.restype = sz
-        L.pqkv_decode_attention.argtypes = [dp, i32, vp, i32, vp, vp, vp, vp, i64, vp, i64, vp, vp, i32, i64,
-                                            vp, f32, vp, vp, vp, sz, vp]
+        L.pqkv_decode_attention.argtypes = [dp, i32, vp, i32, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp, i32,
+                                            i64, vp, f32, vp, vp, vp, sz, vp]
         L.pqkv_decode_attention.restype = i32
         L.pqkv_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                      i64, i64, vp]
@@ -149,20 +149,49 @@ def decode_workspace_bytes(dims: Dims, batch: int, max_hist_len: int) -> int:
     return int(lib().pqkv_decode_workspace_bytes(ctypes.byref(dims), batch, max_hist_len))
 
 
+def _check_numel(name, t, n):
+    if t.numel() < n:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {n}")
+
+
 def decode_attention(dims: Dims, q, codebook_k, codebook_v, codes_k, codes_v, t_cap: int, hist_len,
                      max_hist_len: int, recent_k, recent_v, recent_len, softmax_scale: float, out, lse,
-                     workspace) -> None:
+                     workspace, lut=None) -> None:
     """pqkv_decode_attention.  q: [B, Hq, d]; codes_k/v: uint8 [B, Hkv, t_cap*M];
     hist_len/recent_len: int32 [B] (device); recent_k/v: [B, Hkv, r_cap, d] or None;
-    out: fp32 [B, Hq, d]; lse: fp32 [B, Hq]; workspace: a device tensor (uint8) or None."""
-    _dev(q, codebook_k, codebook_v, codes_k, codes_v, hist_len, recent_k, recent_v, recent_len, out, lse,
+    out: fp32 [B, Hq, d]; lse: fp32 [B, Hq]; workspace: a device tensor (uint8) or None;
+    lut: None (the kernel builds the ad-LUT) or fp32 [B, Hq, M, K] from build_lut
+    (codebook_k may then be None)."""
+    _dev(q, lut, codebook_k, codebook_v, codes_k, codes_v, hist_len, recent_k, recent_v, recent_len, out, lse,
          workspace)
     B = q.shape[0]
-    for t in (q, codebook_k, codebook_v, codes_k, codes_v, out, lse):
-        if not t.is_contiguous():
+    d, M, K, Hq, Hkv = dims.head_dim, dims.n_sub, dims.n_centroids, dims.n_q_heads, dims.n_kv_heads
+    for t in (q, lut, codebook_k, codebook_v, codes_k, codes_v, out, lse, hist_len):
+        if t is not None and not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
-    if hist_len.dtype != torch.int32:
+    if hist_len is not None and hist_len.dtype != torch.int32:
         raise ValueError("hist_len must be int32")
+    _check_numel("q", q, B * Hq * d)
+    _check_numel("out", out, B * Hq * d)
+    _check_numel("lse", lse, B * Hq)
+    if out.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise ValueError("out and lse must be fp32")
+    if max_hist_len > 0:
+        if hist_len is None or codes_k is None or codes_v is None or codebook_v is None:
+            raise ValueError("a history needs hist_len, codes_k/v and codebook_v")
+        _check_numel("hist_len", hist_len, B)
+        _check_numel("codes_k", codes_k, B * Hkv * t_cap * M)
+        _check_numel("codes_v", codes_v, B * Hkv * t_cap * M)
+        for name, cb in (("codebook_k", codebook_k), ("codebook_v", codebook_v)):
+            if cb is None:
+                continue
+            if cb.dtype != torch.float32:
+                raise ValueError(f"{name} must be fp32")
+            _check_numel(name, cb, Hkv * K * d)
+        if lut is not None:
+            if lut.dtype != torch.float32:
+                raise ValueError("lut must be fp32")
+            _check_numel("lut", lut, B * Hq * M * K)
     r_cap = 0 if recent_k is None else recent_k.shape[2]
     rdt = F16 if recent_k is None else _dtype_code(recent_k)
     if recent_k is not None:
@@ -170,11 +199,15 @@ def decode_attention(dims: Dims, q, codebook_k, codebook_v, codes_k, codes_v, t_
             raise ValueError("recent_k/v must be contiguous and recent_len int32")
         if recent_k.shape != recent_v.shape or recent_k.dtype != recent_v.dtype:
             raise ValueError("recent_k and recent_v differ")
+        if tuple(recent_k.shape) != (B, Hkv, r_cap, d):
+            raise ValueError(f"recent_k has shape {tuple(recent_k.shape)}, expected ({B}, {Hkv}, r_cap, {d})")
+        _check_numel("recent_len", recent_len, B)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pqkv_decode_attention", lib().pqkv_decode_attention(
-        ctypes.byref(dims), B, _ptr(q), _dtype_code(q), _ptr(codebook_k), _ptr(codebook_v), _ptr(codes_k),
-        _ptr(codes_v), t_cap, _ptr(hist_len), max_hist_len, _ptr(recent_k), _ptr(recent_v), rdt, r_cap,
-        _ptr(recent_len), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream()))
+        ctypes.byref(dims), B, _ptr(q), _dtype_code(q), _ptr(lut), _ptr(codebook_k), _ptr(codebook_v),
+        _ptr(codes_k), _ptr(codes_v), t_cap, _ptr(hist_len), max_hist_len, _ptr(recent_k), _ptr(recent_v), rdt,
+        r_cap, _ptr(recent_len), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream()))
 
 
 def append_kv(dims: Dims, new_k, new_v, recent_k, recent_v, hist_len_in, recent_len_in, hist_len_out,

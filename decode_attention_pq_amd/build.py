@@ -12,7 +12,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "pqkv")
 LIB = os.path.join(HERE, "libpqkv.so")
-SOURCES = ["encode.hip", "decode.hip", "aux_kernels.hip", "append.hip", "kmeans.hip", "api.cpp"]
+# the decode kernel families come first: they take longest to compile
+DECODE_FAMILIES = ["decode_m64d2.hip", "decode_m64d2_lut.hip", "decode_m32d4.hip", "decode_m32d4_lut.hip",
+                   "decode_m32d2.hip", "decode_m32d2_lut.hip", "decode_m16d4.hip", "decode_m16d4_lut.hip"]
+SOURCES = DECODE_FAMILIES + ["encode.hip", "decode.hip", "aux_kernels.hip", "append.hip", "kmeans.hip", "api.cpp"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are switched off for all device code.
@@ -44,7 +47,7 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link libpqkv.so.  Always recompiles."""
     os.makedirs(OBJ, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 8)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

@@ -98,9 +98,72 @@ DecodePlan plan_decode(const pqkv_dims& d, int32_t batch, int64_t max_hist_len) 
         p.split_tokens = rounds * kTokensPerRound;
     }
     const size_t part = (size_t)batch * d.n_q_heads * p.n_split * p.partial_stride * sizeof(float);
-    p.counters_offset = (part + 255) / 256 * 256;
-    p.workspace_bytes = p.counters_offset + ((size_t)p.units * sizeof(uint32_t) + 255) / 256 * 256;
+    p.partials_offset = decode_counter_bytes(batch, d.n_q_heads);
+    p.workspace_bytes = p.partials_offset + (part + 255) / 256 * 256;
     return p;
+}
+
+pqkv_status check_decode_args(const pqkv_dims* dims, int32_t batch, const void* q, pqkv_dtype q_dtype,
+                              const float* lut, const float* codebook_k, const float* codebook_v,
+                              const uint8_t* codes_k, const uint8_t* codes_v, int64_t t_cap,
+                              const int32_t* hist_len, int64_t max_hist_len, const void* recent_k,
+                              const void* recent_v, pqkv_dtype recent_dtype, int64_t r_cap,
+                              const int32_t* recent_len, float softmax_scale, const float* out,
+                              const float* lse, DecodePlan* plan) {
+    const pqkv_status ds = check_dims(dims);
+    if (ds != PQKV_OK) return ds;
+    if (!dtype_ok(q_dtype) || !dtype_ok(recent_dtype)) return PQKV_ERR_INVALID;
+    if (batch < 0 || max_hist_len < 0 || r_cap < 0 || t_cap < 0) return PQKV_ERR_INVALID;
+    if (max_hist_len > 0 && (t_cap % kTileTokens || max_hist_len > t_cap)) return PQKV_ERR_INVALID;
+    if (r_cap > PQKV_MAX_RECENT) return PQKV_ERR_UNSUPPORTED;
+    // the table is read four centroids at a time
+    if (lut && dims->n_centroids % 4) return PQKV_ERR_UNSUPPORTED;
+    if (batch == 0) return PQKV_OK;
+    // q and the table are read with 8- or 16-byte loads, codebook and recent rows with
+    // 16-byte loads (some straight into LDS)
+    if (!q || !out || !lse || !aligned(q, 16)) return PQKV_ERR_INVALID;
+    if (max_hist_len > 0) {
+        if ((!lut && !codebook_k) || !codebook_v || !codes_k || !codes_v || !hist_len) return PQKV_ERR_INVALID;
+        if (!aligned(codes_k, 16) || !aligned(codes_v, 16) || !aligned(codebook_v, 16)) return PQKV_ERR_INVALID;
+        if ((codebook_k && !aligned(codebook_k, 16)) || (lut && !aligned(lut, 16))) return PQKV_ERR_INVALID;
+    }
+    if (r_cap > 0) {
+        if (!recent_k || !recent_v || !recent_len) return PQKV_ERR_INVALID;
+        if (!aligned(recent_k, 16) || !aligned(recent_v, 16)) return PQKV_ERR_INVALID;
+    }
+    if (!(softmax_scale == softmax_scale)) return PQKV_ERR_INVALID;  // NaN
+    if ((int64_t)batch * dims->n_q_heads > 0x7fffffffLL) return PQKV_ERR_UNSUPPORTED;
+    *plan = plan_decode(*dims, batch, max_hist_len);
+    if (plan->n_split > kMaxSplits || plan->units * plan->n_split > 0x7fffffffLL - 8) return PQKV_ERR_UNSUPPORTED;
+    return PQKV_OK;
+}
+
+// Kernel arguments of a checked call.
+DecodeArgs decode_args(const void* q, const float* lut, const float* codebook_k, const float* codebook_v,
+                       const uint8_t* codes_k, const uint8_t* codes_v, int64_t t_cap, const int32_t* hist_len,
+                       int64_t max_hist_len, const void* recent_k, const void* recent_v, int64_t r_cap,
+                       const int32_t* recent_len, float softmax_scale, float* out, float* lse,
+                       uint32_t* counters, float* partials) {
+    DecodeArgs a;
+    a.q = q;
+    a.lut = max_hist_len > 0 ? lut : nullptr;
+    a.cb_k = a.lut ? nullptr : codebook_k;
+    a.cb_v = codebook_v;
+    a.codes_k = codes_k;
+    a.codes_v = codes_v;
+    a.t_cap = t_cap;
+    a.hist_len = max_hist_len > 0 ? hist_len : nullptr;  // no history: the kernel takes 0
+    a.max_hist = max_hist_len;
+    a.rk = r_cap > 0 ? recent_k : nullptr;
+    a.rv = r_cap > 0 ? recent_v : nullptr;
+    a.r_cap = r_cap;
+    a.recent_len = r_cap > 0 ? recent_len : nullptr;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.out = out;
+    a.lse = lse;
+    a.counters = counters;
+    a.partials = partials;
+    return a;
 }
 
 }  // namespace pqkv
@@ -160,7 +223,7 @@ size_t pqkv_decode_workspace_bytes(const pqkv_dims* dims, int32_t batch, int64_t
 }
 
 pqkv_status pqkv_decode_attention(const pqkv_dims* dims, int32_t batch, const void* q,
-                                  pqkv_dtype q_dtype, const float* codebook_k,
+                                  pqkv_dtype q_dtype, const float* lut, const float* codebook_k,
                                   const float* codebook_v, const uint8_t* codes_k,
                                   const uint8_t* codes_v, int64_t t_cap, const int32_t* hist_len,
                                   int64_t max_hist_len, const void* recent_k, const void* recent_v,
@@ -168,43 +231,18 @@ pqkv_status pqkv_decode_attention(const pqkv_dims* dims, int32_t batch, const vo
                                   const int32_t* recent_len, float softmax_scale, float* out,
                                   float* lse, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
-    const pqkv_status ds = check_dims(dims);
-    if (ds != PQKV_OK) return ds;
-    if (!dtype_ok(q_dtype) || !dtype_ok(recent_dtype)) return PQKV_ERR_INVALID;
-    if (batch < 0 || max_hist_len < 0 || r_cap < 0 || t_cap < 0) return PQKV_ERR_INVALID;
-    if (max_hist_len > 0 && (t_cap % kTileTokens || max_hist_len > t_cap)) return PQKV_ERR_INVALID;
-    if (r_cap > PQKV_MAX_RECENT) return PQKV_ERR_UNSUPPORTED;
-    if (batch == 0) return PQKV_OK;
-    if (!q || !out || !lse) return PQKV_ERR_INVALID;
-    if (max_hist_len > 0) {
-        if (!codebook_k || !codebook_v || !codes_k || !codes_v || !hist_len) return PQKV_ERR_INVALID;
-        if (!aligned(codes_k, 16) || !aligned(codes_v, 16)) return PQKV_ERR_INVALID;
-    }
-    if (r_cap > 0 && (!recent_k || !recent_v || !recent_len)) return PQKV_ERR_INVALID;
-    if (!(softmax_scale == softmax_scale)) return PQKV_ERR_INVALID;  // NaN
-    if ((int64_t)batch * dims->n_q_heads > 0x7fffffffLL) return PQKV_ERR_UNSUPPORTED;
-    const DecodePlan plan = plan_decode(*dims, batch, max_hist_len);
-    if (plan.n_split > kMaxSplits || plan.units * plan.n_split > 0x7fffffffLL - 8) return PQKV_ERR_UNSUPPORTED;
+    DecodePlan plan{};
+    const pqkv_status st =
+        check_decode_args(dims, batch, q, q_dtype, lut, codebook_k, codebook_v, codes_k, codes_v, t_cap, hist_len,
+                          max_hist_len, recent_k, recent_v, recent_dtype, r_cap, recent_len, softmax_scale, out,
+                          lse, &plan);
+    if (st != PQKV_OK || batch == 0) return st;
     if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned(workspace, 256)) return PQKV_ERR_WORKSPACE;
-
-    DecodeArgs a;
-    a.q = q;
-    a.cb_k = codebook_k;
-    a.cb_v = codebook_v;
-    a.codes_k = codes_k;
-    a.codes_v = codes_v;
-    a.t_cap = t_cap;
-    a.hist_len = hist_len;
-    a.max_hist = max_hist_len;
-    a.rk = r_cap > 0 ? recent_k : nullptr;
-    a.rv = r_cap > 0 ? recent_v : nullptr;
-    a.r_cap = r_cap;
-    a.recent_len = r_cap > 0 ? recent_len : nullptr;
-    a.scale_log2 = softmax_scale * 1.4426950408889634f;
-    a.out = out;
-    a.lse = lse;
-    a.partials = static_cast<float*>(workspace);
-    a.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.counters_offset);
+    // the workspace holds the counters at byte 0 and the partials after them
+    const DecodeArgs a = decode_args(q, lut, codebook_k, codebook_v, codes_k, codes_v, t_cap, hist_len,
+                                     max_hist_len, recent_k, recent_v, r_cap, recent_len, softmax_scale, out, lse,
+                                     static_cast<uint32_t*>(workspace),
+                                     reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.partials_offset));
     return hip_status(launch_decode(*dims, batch, q_dtype, recent_dtype, plan, a, stream));
 }
 

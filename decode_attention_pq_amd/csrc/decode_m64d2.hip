@@ -1,0 +1,11 @@
+// Decode kernel builds for 64 subspaces of dimension 2, ad-LUT built in the kernel.
+#include "decode_kernel.h"
+
+namespace pqkv {
+
+hipError_t launch_decode_m64d2(const pqkv_dims& d, int32_t batch, pqkv_dtype qt, pqkv_dtype rt, const DecodePlan& plan,
+                         const DecodeArgs& a, hipStream_t stream) {
+    return launch_family<64, 2, false>(d, batch, qt, rt, plan, a, stream);
+}
+
+}  // namespace pqkv

@@ -41,14 +41,23 @@ struct DecodePlan {
     int64_t split_tokens;
     int partial_stride;  // floats per partial record: d outputs + max + sum, padded
     int64_t units;       // (sequence, kv head, group) units, one completion counter each
-    size_t counters_offset;  // byte offset of the counters inside the workspace
+    size_t partials_offset;  // byte offset of the partials (the counters sit at byte 0)
     size_t workspace_bytes;
 };
 
 DecodePlan plan_decode(const pqkv_dims& d, int32_t batch, int64_t max_hist_len);
 
+// Completion counters at the start of a workspace: one u32 slot per (sequence,
+// query head), which bounds the units of every plan, rounded up to 256 bytes.  The
+// offset of the partials after them depends only on batch and n_q_heads, so a
+// workspace zeroed once serves every later call whatever its max_hist_len.
+inline size_t decode_counter_bytes(int32_t batch, int32_t n_q_heads) {
+    return ((size_t)batch * (size_t)n_q_heads * sizeof(uint32_t) + 255) / 256 * 256;
+}
+
 struct DecodeArgs {
     const void* q;
+    const float* lut;  // nullable: the materialised table [B][Hq][M][K], unscaled
     const float* cb_k;
     const float* cb_v;
     const uint8_t* codes_k;
@@ -69,5 +78,23 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const pqkv_dims& d, int32_t batch, pqkv_dtype qt, pqkv_dtype rt,
                          const DecodePlan& plan, const DecodeArgs& a, hipStream_t stream);
+
+// Host-side validation shared by the decode entry points: the status the call
+// returns before any launch (PQKV_OK if it may go ahead), with the plan filled in.
+pqkv_status check_decode_args(const pqkv_dims* dims, int32_t batch, const void* q, pqkv_dtype q_dtype,
+                              const float* lut, const float* codebook_k, const float* codebook_v,
+                              const uint8_t* codes_k, const uint8_t* codes_v, int64_t t_cap,
+                              const int32_t* hist_len, int64_t max_hist_len, const void* recent_k,
+                              const void* recent_v, pqkv_dtype recent_dtype, int64_t r_cap,
+                              const int32_t* recent_len, float softmax_scale, const float* out,
+                              const float* lse, DecodePlan* plan);
+
+// Kernel arguments of a call that check_decode_args accepted: the completion counters
+// (one u32 per (sequence, query head), zero between calls) and the partials.
+DecodeArgs decode_args(const void* q, const float* lut, const float* codebook_k, const float* codebook_v,
+                       const uint8_t* codes_k, const uint8_t* codes_v, int64_t t_cap, const int32_t* hist_len,
+                       int64_t max_hist_len, const void* recent_k, const void* recent_v, int64_t r_cap,
+                       const int32_t* recent_len, float softmax_scale, float* out, float* lse,
+                       uint32_t* counters, float* partials);
 
 }  // namespace pqkv

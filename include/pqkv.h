@@ -116,8 +116,9 @@ pqkv_status pqkv_encode(const pqkv_dims* dims, const void* x, pqkv_dtype x_dtype
  *   q           device [batch][Hq][d] in q_dtype (F16 or F32), dense.
  *   codebook_k  device fp32 [Hkv][K][M][d_sub].
  *   lut         device fp32 [batch][Hq][M][K], dense, written whole.
- * pqkv_decode_attention does not need this table: it builds the same table in
- * on-chip memory.  Errors as for pqkv_encode.
+ * pqkv_decode_attention takes this table through its `lut` argument; given NULL
+ * there, it builds the same table itself in on-chip memory.  Errors as for
+ * pqkv_encode.
  */
 pqkv_status pqkv_build_lut(const pqkv_dims* dims, int32_t batch, const void* q, pqkv_dtype q_dtype,
                            const float* codebook_k, float* lut, hipStream_t stream);
@@ -143,31 +144,44 @@ size_t pqkv_decode_workspace_bytes(const pqkv_dims* dims, int32_t batch, int64_t
  *     lse  = mu + ln sum_i exp(s_i - mu).
  * A row with no tokens gets out = 0 and lse = -inf.
  *
- *   q             device [batch][Hq][d], q_dtype, dense.
- *   codebook_k/v  device fp32 [Hkv][K][M][d_sub].
+ *   q             device [batch][Hq][d], q_dtype, dense, 16-byte aligned.
+ *   lut           NULL: the kernel builds the ad-LUT from q and codebook_k in on-chip
+ *                 memory.  Otherwise device fp32 [batch][Hq][M][K], 16-byte aligned: the
+ *                 unscaled table pqkv_build_lut writes (entry (b, hq, m, c) = q_m . centroid c
+ *                 of subspace m of kv head hq / g), read in place of building it; the
+ *                 history scores are then softmax_scale times sums of its entries, and
+ *                 codebook_k is not read (it may be NULL).  Needs K % 4 == 0.
+ *   codebook_k/v  device fp32 [Hkv][K][M][d_sub], 16-byte aligned.
  *   codes_k/v     device uint8 cache planes (layout above), batch*Hkv planes of t_cap*M
  *                 bytes, 16-byte aligned; only tokens < hist_len[b] are read.
- *   hist_len      device int32 [batch], each in [0, max_hist_len].
+ *   hist_len      device int32 [batch], each in [0, max_hist_len]; may be NULL if
+ *                 max_hist_len == 0 (every history is then empty).
  *   max_hist_len  host bound on hist_len, <= t_cap; sizes the split-over-tokens grid.
- *   recent_k/v    device [batch][Hkv][r_cap][d] in recent_dtype, dense; may be NULL if r_cap == 0.
+ *   recent_k/v    device [batch][Hkv][r_cap][d] in recent_dtype, dense, 16-byte aligned;
+ *                 may be NULL if r_cap == 0.
  *   recent_len    device int32 [batch], each in [0, r_cap]; may be NULL if r_cap == 0.
  *   r_cap         0..PQKV_MAX_RECENT.
  *   out           device fp32 [batch][Hq][d];  lse device fp32 [batch][Hq] (natural log).
  *   workspace     device, >= pqkv_decode_workspace_bytes(dims, batch, max_hist_len) bytes,
- *                 256-byte aligned.  It must be zero-filled before the first call that uses
- *                 it (e.g. one hipMemset); every call leaves it ready for the next one.  It
- *                 holds per-split partial results and per-(sequence, kv head) completion
- *                 counters, so calls sharing one workspace must be ordered on one stream.
+ *                 256-byte aligned.  It starts with completion counters (4 bytes per
+ *                 (sequence, query head), rounded up to 256 bytes), followed by per-split
+ *                 partial results.  The counters must be zero before the first call that
+ *                 uses the workspace (e.g. one hipMemset of the whole buffer); every call
+ *                 returns them to zero.  Their size depends only on batch and n_q_heads, so
+ *                 one zeroed workspace serves every later call whose batch * n_q_heads is
+ *                 at most that of the first, whatever its max_hist_len, as long as it is
+ *                 large enough; zero it again before a call with a larger batch * n_q_heads.
+ *                 Calls sharing one workspace must be ordered on one stream.
  * The call allocates nothing, records no memset and never waits on the host, so
  * it may be captured in a HIP graph and replayed with new device-side q and
  * lengths (max_hist_len, fixed at capture, must still bound them).
  * Device-side lengths outside their bounds are clamped to them.  Errors: INVALID
- * for null pointers, negative sizes, max_hist_len > t_cap, bad dtype;
- * UNSUPPORTED for dims outside the ranges above or r_cap > PQKV_MAX_RECENT;
- * WORKSPACE for a missing or short workspace.
+ * for null pointers, misaligned pointers, negative sizes, max_hist_len > t_cap, bad
+ * dtype; UNSUPPORTED for dims outside the ranges above, r_cap > PQKV_MAX_RECENT, or a
+ * lut with K % 4 != 0; WORKSPACE for a missing, short or misaligned workspace.
  */
 pqkv_status pqkv_decode_attention(const pqkv_dims* dims, int32_t batch, const void* q,
-                                  pqkv_dtype q_dtype, const float* codebook_k,
+                                  pqkv_dtype q_dtype, const float* lut, const float* codebook_k,
                                   const float* codebook_v, const uint8_t* codes_k,
                                   const uint8_t* codes_v, int64_t t_cap, const int32_t* hist_len,
                                   int64_t max_hist_len, const void* recent_k, const void* recent_v,

@@ -180,6 +180,11 @@ def encode(x, codebook):
 
 
 def ambiguous(d1, d2):
+    """The tie tolerance of the encode comparison: the runner-up distance d2 lies less
+    than 1e-5 * max(1, d1) above the best one d1.  The page fixes no tolerance; the
+    reading is a relative band floored at 1, because an absolute 1e-5 is below fp32
+    resolution for outlier subvectors (d1 of 1e2 to 1e5).  Pinned at its boundaries
+    by constructed pairs in the tests."""
     return (d2 - d1) < AMBIGUITY_REL * np.maximum(1.0, d1)
 
 

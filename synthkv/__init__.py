@@ -18,10 +18,11 @@ then rounded to fp16.  The clustered outliers of the same figure are not
 modelled.
 
 Random streams: every array comes from its own
-``SeedSequence([seed, layer, tensor, purpose, b])``: normals from torch's CPU
-generator seeded by it (same values for any thread count), everything else
-from ``np.random.default_rng`` on it, so arrays are independent of generation
-order.
+``SeedSequence([seed, layer, tensor, purpose, b])`` -- K/V values from one per
+1024-token chunk, ``SeedSequence([seed, layer, tensor, purpose, b, chunk])`` --:
+normals from torch's CPU generator seeded by it (same values for any thread
+count), everything else from ``np.random.default_rng`` on it, so arrays are
+independent of generation order, and a sample of chunks can be drawn alone.
 """
 from __future__ import annotations
 
@@ -173,18 +174,51 @@ def bernoulli_positions(g: np.random.Generator, n: int, p: float) -> np.ndarray:
     return np.concatenate(out)
 
 
-def kv_values(w: Workload, layer: int, tensor: str, purpose: str, n_tokens: int, b: int = 0) -> np.ndarray:
-    """Token-major K or V values [n_tokens, n_kv_heads, head_dim] in the workload dtype."""
-    ss = np.random.SeedSequence([w.seed, layer, TENSOR[tensor], PURPOSE[purpose], b])
-    x = _normal(ss, (n_tokens, w.n_kv_heads, w.head_dim))
-    if w.outliers:
-        ch = outlier_channels(w, layer, tensor)
-        for h in range(w.n_kv_heads):
-            x[:, h, ch[h]] *= CHANNEL_SCALE
-        g = np.random.default_rng(ss.spawn(1)[0])
-        flat = x.reshape(-1)
-        flat[bernoulli_positions(g, flat.size, POINT_PROB)] *= POINT_SCALE
-    return _to_dtype(x, w.np_dtype)
+# Values are drawn in chunks of this many tokens, each from a stream of its own, so a
+# sample of chunks can be drawn without the rest (same values either way).
+CHUNK_TOKENS = 1024
+
+
+def n_chunks(n_tokens: int) -> int:
+    return -(-n_tokens // CHUNK_TOKENS)
+
+
+def kv_values(w: Workload, layer: int, tensor: str, purpose: str, n_tokens: int, b: int = 0,
+              chunks=None) -> np.ndarray:
+    """Token-major K or V values [n_tokens, n_kv_heads, head_dim] in the workload dtype.
+
+    Chunk c (tokens [1024c, 1024c + 1024)) comes from
+    SeedSequence([seed, layer, tensor, purpose, b, c]).  With `chunks` (a sorted list of
+    chunk indices) only those chunks are drawn and concatenated, in order."""
+    ids = list(range(n_chunks(n_tokens))) if chunks is None else [int(c) for c in chunks]
+    sizes = [min(CHUNK_TOKENS, n_tokens - c * CHUNK_TOKENS) for c in ids]
+    assert all(n > 0 for n in sizes), "chunk index past the end"
+    out = np.empty((sum(sizes), w.n_kv_heads, w.head_dim), dtype=w.np_dtype)
+    ch = outlier_channels(w, layer, tensor) if w.outliers else None
+    pos = 0
+    for c, n in zip(ids, sizes):
+        ss = np.random.SeedSequence([w.seed, layer, TENSOR[tensor], PURPOSE[purpose], b, c])
+        x = _normal(ss, (n, w.n_kv_heads, w.head_dim))
+        if w.outliers:
+            x[:, np.arange(w.n_kv_heads)[:, None], ch] *= CHANNEL_SCALE
+            g = np.random.default_rng(ss.spawn(1)[0])
+            flat = x.reshape(-1)
+            flat[bernoulli_positions(g, flat.size, POINT_PROB)] *= POINT_SCALE
+        out[pos:pos + n] = _to_dtype(x, w.np_dtype)
+        pos += n
+    return out
+
+
+def sample_chunks(seed: int, n_tokens: int, fraction: float = 0.125) -> list:
+    """A seeded sorted sample of ceil(fraction * chunks) chunk indices (at least one)."""
+    n = n_chunks(n_tokens)
+    k = max(1, -(-int(round(fraction * 1e6)) * n // 1000000))
+    return sorted(int(c) for c in np.random.default_rng(seed).choice(n, size=min(k, n), replace=False))
+
+
+def chunk_tokens(chunks, n_tokens: int) -> np.ndarray:
+    """The token positions the given chunks cover, in order."""
+    return np.concatenate([np.arange(c * CHUNK_TOKENS, min((c + 1) * CHUNK_TOKENS, n_tokens)) for c in chunks])
 
 
 def queries(w: Workload, layer: int = 0) -> np.ndarray:
@@ -201,9 +235,10 @@ def recent_kv(w: Workload, layer: int, tensor: str) -> np.ndarray:
     return out
 
 
-def history_kv(w: Workload, layer: int, tensor: str, b: int) -> np.ndarray:
-    """PQ-history values of sequence b, token-major [hist_len[b], n_kv_heads, head_dim]."""
-    return kv_values(w, layer, tensor, "history", w.hist_len[b], b)
+def history_kv(w: Workload, layer: int, tensor: str, b: int, chunks=None) -> np.ndarray:
+    """PQ-history values of sequence b, token-major [hist_len[b], n_kv_heads, head_dim]
+    (only the given 1024-token chunks, concatenated, with `chunks`)."""
+    return kv_values(w, layer, tensor, "history", w.hist_len[b], b, chunks)
 
 
 def calibration_kv(w: Workload, layer: int, tensor: str) -> np.ndarray:

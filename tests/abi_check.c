@@ -36,8 +36,22 @@ int main(void) {
         EXPECT(pqkv_append_kv(&d, 1, fake, fake, fake, fake, PQKV_F16, 128, lens, lens + 1, lens, lens + 3, 64, fake,
                               fake, fake, fake, 4096, 100, NULL) == PQKV_ERR_INVALID); /* out aliases in */
     }
-    EXPECT(pqkv_decode_attention(&d, 1, fake, PQKV_F16, fake, fake, fake, fake, 32768, fake, 32768, fake, fake,
+    EXPECT(pqkv_decode_attention(&d, 1, fake, PQKV_F16, NULL, fake, fake, fake, fake, 32768, fake, 32768, fake,
+                                 fake, PQKV_F16, 128, fake, 0.088f, fake, fake, NULL, 0, NULL) == PQKV_ERR_WORKSPACE);
+    /* a history needs its lengths; with no history they may be NULL */
+    EXPECT(pqkv_decode_attention(&d, 1, fake, PQKV_F16, NULL, fake, fake, fake, fake, 32768, NULL, 32768, fake,
+                                 fake, PQKV_F16, 128, fake, 0.088f, fake, fake, fake, 1 << 20, NULL) == PQKV_ERR_INVALID);
+    EXPECT(pqkv_decode_attention(&d, 1, fake, PQKV_F16, NULL, NULL, NULL, NULL, NULL, 0, NULL, 0, fake, fake,
                                  PQKV_F16, 128, fake, 0.088f, fake, fake, NULL, 0, NULL) == PQKV_ERR_WORKSPACE);
+    /* misaligned query */
+    EXPECT(pqkv_decode_attention(&d, 1, (char*)fake + 4, PQKV_F16, NULL, fake, fake, fake, fake, 32768, fake, 32768,
+                                 fake, fake, PQKV_F16, 128, fake, 0.088f, fake, fake, fake, 1 << 20,
+                                 NULL) == PQKV_ERR_INVALID);
+    /* a table in place of the key codebook */
+    EXPECT(pqkv_decode_attention(&d, 1, fake, PQKV_F16, fake, NULL, fake, fake, fake, 32768, fake, 32768, fake,
+                                 fake, PQKV_F16, 128, fake, 0.088f, fake, fake, NULL, 0, NULL) == PQKV_ERR_WORKSPACE);
+    /* 4096 tokens, 32 heads: 8 splits per head; the counters (one per query head) come first */
+    EXPECT(pqkv_decode_workspace_bytes(&d, 1, 4096) == (size_t)(256 + 32 * 8 * 132 * 4));
     printf(fails ? "abi_check: %d failures\n" : "abi_check: ok\n", fails);
     return fails != 0;
 }

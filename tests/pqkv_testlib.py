@@ -39,8 +39,12 @@ def dims_for(head_dim, d_sub, K, Hq, Hkv):
 
 
 def run_gpu_decode(dims, q, cb_k, cb_v, planes_k, planes_v, t_cap, hist_len, recent_k, recent_v, recent_len,
-                   scale, max_hist=None, out_fill=np.nan):
-    """Everything numpy in, numpy out; planes_* already in the cache layout."""
+                   scale, max_hist=None, out_fill=np.nan, lut="none", workspace=None):
+    """Everything numpy in, numpy out; planes_* already in the cache layout.
+
+    lut: "none" (the kernel builds the ad-LUT), "gpu" (pqkv_build_lut's table from q and
+    cb_k is passed in, and cb_k is not), or a numpy table [B, Hq, M, K] to pass in.
+    workspace: a device tensor to use (and keep), else a fresh zeroed one."""
     import torch
 
     import decode_attention_pq_amd as P
@@ -56,11 +60,22 @@ def run_gpu_decode(dims, q, cb_k, cb_v, planes_k, planes_v, t_cap, hist_len, rec
         rl = to_dev(np.asarray(recent_len, np.int32))
     else:
         rk = rv = rl = None
+    table = None
+    if isinstance(lut, str) and lut == "gpu":
+        table = torch.full((B, Hq, dims.head_dim // dims.d_sub, dims.n_centroids), np.nan, dtype=torch.float32,
+                           device="cuda")
+        P.build_lut(dims, qd, cbk, table)
+        cbk = None
+    elif not isinstance(lut, str):
+        table = to_dev(np.asarray(lut, np.float32))
+        cbk = None
     out = torch.full((B, Hq, d), out_fill, dtype=torch.float32, device="cuda")
     lse = torch.full((B, Hq), out_fill, dtype=torch.float32, device="cuda")
-    nbytes = P.decode_workspace_bytes(dims, B, max_hist)
-    ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
-    P.decode_attention(dims, qd, cbk, cbv, ck, cv, t_cap, hl, max_hist, rk, rv, rl, scale, out, lse, ws)
+    if workspace is None:
+        nbytes = P.decode_workspace_bytes(dims, B, max_hist)
+        workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    P.decode_attention(dims, qd, cbk, cbv, ck, cv, t_cap, hl, max_hist, rk, rv, rl, scale, out, lse, workspace,
+                       lut=table)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy()
 

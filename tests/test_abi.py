@@ -71,9 +71,9 @@ def test_decode_validation(P):
     assert ws_need > 0
 
     def call(dims=dims, batch=1, t_cap=32768, maxh=32768, r_cap=128, ws=FAKE, wsb=None, codes=FAKE, qdt=0,
-             scale=0.088):
+             scale=0.088, q=FAKE, lut=None, cbk=FAKE, cbv=FAKE, hist=FAKE, rk=FAKE):
         return L.pqkv_decode_attention(
-            _d(P, *dims), batch, FAKE, qdt, FAKE, FAKE, codes, codes, t_cap, FAKE, maxh, FAKE, FAKE, 0, r_cap,
+            _d(P, *dims), batch, q, qdt, lut, cbk, cbv, codes, codes, t_cap, hist, maxh, rk, FAKE, 0, r_cap,
             FAKE, scale, FAKE, FAKE, ws, ws_need if wsb is None else wsb, None)
 
     assert call(ws=None) == 3
@@ -89,12 +89,20 @@ def test_decode_validation(P):
     assert call(scale=float("nan")) == 1
     assert call(dims=(128, 2, 1, 32, 32)) == 2            # K < 2
     assert call(dims=(128, 2, 256, 0, 32)) == 1
+    assert call(hist=None) == 1                           # lengths needed when there is a history
+    assert call(q=ctypes.c_void_p(0x10008)) == 1          # q not 16-byte aligned
+    assert call(cbv=ctypes.c_void_p(0x10008)) == 1        # value codebook not 16-byte aligned
+    assert call(rk=ctypes.c_void_p(0x10004)) == 1         # recent rows not 16-byte aligned
+    assert call(cbk=None) == 1                            # no key codebook and no table
+    assert call(cbk=None, lut=FAKE, wsb=ws_need - 1) == 3  # the table stands in for the key codebook
+    assert call(lut=ctypes.c_void_p(0x10004)) == 1        # table not 16-byte aligned
+    assert call(dims=(128, 2, 250, 32, 32), lut=FAKE) == 2  # the table is read 4 centroids at a time
 
 
 def test_workspace_formula(P):
     L = P.lib()
-    # partials (132 floats per query head and split) padded to 256 bytes, then one
-    # u32 completion counter per (sequence, kv head, query-head group), padded
+    # one u32 completion counter per (sequence, query head) padded to 256 bytes, then
+    # the partials (132 floats per query head and split), padded
     # LLaMA-2-7B shape at 32K context: 32 kv heads, one query head each, 8 splits of 4096 tokens
     assert L.pqkv_decode_workspace_bytes(_d(P, 128, 2, 256, 32, 32), 1, 32768) == 32 * 8 * 132 * 4 + 256
     # no history: one split per unit for the recent window
@@ -106,8 +114,9 @@ def test_workspace_formula(P):
 
 
 def test_split_plan_choices(P):
-    """The split plan, read back through the workspace size (partials of 132 floats per
-    query head and split, padded to 256 bytes, then one u32 counter per unit, padded)."""
+    """The split plan, read back through the workspace size (one u32 counter per
+    sequence and query head, padded to 256 bytes, then the partials of 132 floats per
+    query head and split, padded)."""
     L = P.lib()
     ws = lambda dims, batch, maxh: L.pqkv_decode_workspace_bytes(_d(P, *dims), batch, maxh)
     pad = lambda n: -(-n // 256) * 256
@@ -125,7 +134,7 @@ def test_split_plan_choices(P):
     # 5,000,000 tokens need more than 512 splits even at 16 rounds: refused
     need = ws((128, 2, 256, 1, 1), 1, 5000000)
     assert need == pad(611 * 528) + 256
-    assert L.pqkv_decode_attention(_d(P, 128, 2, 256, 1, 1), 1, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 5000000, FAKE,
+    assert L.pqkv_decode_attention(_d(P, 128, 2, 256, 1, 1), 1, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, 5000000, FAKE,
                                    5000000, FAKE, FAKE, 0, 0, FAKE, 0.088, FAKE, FAKE, FAKE, need, None) == 2
 
 

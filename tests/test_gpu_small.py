@@ -205,6 +205,95 @@ def test_decode_matches_oracle(case):
         check_attention(out2, lse2, ref_out, ref_lse)
 
 
+LUT_CASES = [i for i, c in enumerate(DECODE_CASES) if c[2] % 4 == 0 and max(c[5]) > 0]
+
+
+@pytest.mark.parametrize("i", LUT_CASES, ids=[f"case{i}" for i in LUT_CASES])
+def test_decode_with_materialised_lut(i):
+    """pqkv_build_lut's table passed to pqkv_decode_attention in place of the key
+    codebook (the ad-LUT built first, then read for every token), against the
+    oracle's exact attention."""
+    d, dsub, K, Hq, Hkv, hist, rec, r_cap, dt = DECODE_CASES[i]
+    B = len(hist)
+    M = d // dsub
+    t_cap = max(64, -(-max(hist) // 64) * 64)
+    seed = sum(hist) + 31 * K + d + 7
+    q = synthkv.small_normal(seed, (B, Hq, d), dt)
+    cbk = _codebook(seed + 1, Hkv, K, M, dsub, 1.0)
+    cbv = _codebook(seed + 2, Hkv, K, M, dsub, 1.0)
+    ck = synthkv.small_codes(seed + 3, (B, Hkv, t_cap, M), K)
+    cv = synthkv.small_codes(seed + 4, (B, Hkv, t_cap, M), K)
+    rk = synthkv.small_normal(seed + 5, (B, Hkv, r_cap, d), dt)
+    rv = synthkv.small_normal(seed + 6, (B, Hkv, r_cap, d), dt)
+    scale = softmax_scale(d)
+    ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, hist, rk, rv, rec, scale)
+    pk, pv = oracle.tile_codes(ck, t_cap), oracle.tile_codes(cv, t_cap)
+    dims = dims_for(d, dsub, K, Hq, Hkv)
+    r = (rk, rv) if r_cap else (None, None)
+    out, lse = run_gpu_decode(dims, q, cbk, cbv, pk, pv, t_cap, hist, r[0], r[1], rec, scale, lut="gpu")
+    check_attention(out, lse, ref_out, ref_lse)
+    # the oracle's own table (fp64, rounded to fp32) gives the same result
+    out2, lse2 = run_gpu_decode(dims, q, cbk, cbv, pk, pv, t_cap, hist, r[0], r[1], rec, scale,
+                                lut=oracle.lut(q, cbk, Hq // Hkv))
+    check_attention(out2, lse2, ref_out, ref_lse)
+
+
+def test_decode_recent_window_only_without_lengths():
+    """No history (max_hist_len 0): hist_len, codes and codebooks may all be NULL."""
+    import torch
+
+    import decode_attention_pq_amd as P
+
+    d, dsub, K, Hq, Hkv, B, r_cap = 128, 2, 256, 8, 4, 3, 16
+    rec = [16, 0, 5]
+    q = synthkv.small_normal(91, (B, Hq, d), np.float16)
+    rk = synthkv.small_normal(92, (B, Hkv, r_cap, d), np.float16)
+    rv = synthkv.small_normal(93, (B, Hkv, r_cap, d), np.float16)
+    scale = softmax_scale(d)
+    M = d // dsub
+    empty = np.zeros((B, Hkv, 64, M), np.uint8)
+    cb = np.zeros((Hkv, K, M, dsub), np.float32)
+    ref_out, ref_lse = oracle.decode_exact(q, cb, cb, empty, empty, [0] * B, rk, rv, rec, scale)
+    dims = dims_for(d, dsub, K, Hq, Hkv)
+    out = torch.full((B, Hq, d), np.nan, device="cuda")
+    lse = torch.full((B, Hq), np.nan, device="cuda")
+    ws = torch.zeros(P.decode_workspace_bytes(dims, B, 0), dtype=torch.uint8, device="cuda")
+    P.decode_attention(dims, to_dev(q), None, None, None, None, 0, None, 0, to_dev(rk), to_dev(rv),
+                       to_dev(np.asarray(rec, np.int32)), scale, out, lse, ws)
+    torch.cuda.synchronize()
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse)
+
+
+def test_workspace_reuse_when_max_hist_len_changes():
+    """One zeroed workspace across calls whose split plans differ (4096 tokens: 8
+    splits per head; 4160: 5 splits; and back), each checked against the oracle: the
+    completion counters sit at a fixed place, so no call reads another's partials as
+    counters."""
+    import torch
+
+    import decode_attention_pq_amd as P
+
+    d, dsub, K, H, B = 128, 2, 256, 32, 1
+    M = d // dsub
+    dims = dims_for(d, dsub, K, H, H)
+    t_cap = 4224
+    sizes = [P.decode_workspace_bytes(dims, B, T) for T in (4096, 4160)]
+    assert sizes[0] != sizes[1], "the two lengths should take different split plans"
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device="cuda")
+    scale = softmax_scale(d)
+    for it, T in enumerate((4096, 4160, 4096, 4160)):
+        q = synthkv.small_normal(700 + it, (B, H, d), np.float16)
+        cbk = _codebook(710 + it, H, K, M, dsub, 1.0)
+        cbv = _codebook(720 + it, H, K, M, dsub, 1.0)
+        ck = synthkv.small_codes(730 + it, (B, H, t_cap, M), K)
+        cv = synthkv.small_codes(740 + it, (B, H, t_cap, M), K)
+        ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, [T], np.zeros((B, H, 0, d), np.float16),
+                                               np.zeros((B, H, 0, d), np.float16), [0], scale)
+        out, lse = run_gpu_decode(dims, q, cbk, cbv, oracle.tile_codes(ck, t_cap), oracle.tile_codes(cv, t_cap),
+                                  t_cap, [T], None, None, [0], scale, max_hist=T, workspace=ws)
+        check_attention(out, lse, ref_out, ref_lse)
+
+
 def test_tiny_workload_end_to_end():
     """The Tiny workload: codebooks fit by 10 Lloyd iterations on its own history,
     GPU encode bit-exact with the oracle, GPU decode within tolerance."""

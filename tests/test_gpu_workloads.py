@@ -4,8 +4,17 @@ whole history or prefill, one pqkv_decode_attention call per layer with the
 workload's own batch, lengths and max_hist_len).
 
 Where the oracle cannot afford every output at full size it checks a seeded
-sample of them (encode: every s-th token of every sequence, all heads and
-subspaces); the stride is printed with the result.  Decode inputs are codes
+sample of them, printed with the result:
+  * the batched workload: every sequence of the 16 x 8192 prefill, every 8th
+    token from an offset that rotates with the sequence (so every token position
+    is checked in two sequences);
+  * the 32-layer workload: every layer's 32768-token prefill, encoded in one
+    launch, checked on every 8th token from an offset that rotates with the layer
+    (every position in four layers); and a seeded eighth of the 1024-token chunks
+    of every (layer, sequence) history, all of their tokens checked.
+Each encode check reports how many codes fall in the ambiguity band under the
+relative reading the comparison uses (D2 - D1 < 1e-5 * max(1, D1)) and under an
+absolute 1e-5.  Decode inputs are codes
 the oracle itself produced, or seeded random codes where encoding the whole
 history on the CPU would take minutes -- attention parity does not depend on
 how valid codes were obtained, and encode parity is checked separately.
@@ -28,7 +37,7 @@ def _log(msg):
     print(f"[workload] {msg}", flush=True)
 
 
-@functools.lru_cache(maxsize=4)
+@functools.lru_cache(maxsize=16)
 def _fitted(name, layer, tensor):
     w = synthkv.WORKLOADS[name]
     t0 = time.time()
@@ -53,15 +62,20 @@ def _gpu_encode_seq(w, x, cb, t_cap, t_start=0):
     return planes[0].cpu().numpy()
 
 
-def _check_sampled_codes(w, x, cb, planes, t_cap, stride, t_start=0):
-    """Oracle-encode every `stride`-th token and compare with the GPU planes."""
-    idx = np.arange(0, x.shape[0], stride)
+def _check_sampled_codes(w, x, cb, planes, t_cap, stride, t_start=0, offset=0, positions=None, what=""):
+    """Oracle-encode every `stride`-th token of x (from `offset`) and compare with the
+    GPU planes; x's token i sits at plane position t_start + i, or positions[i].
+    Returns (oracle codes, codes in the relative band, in an absolute 1e-5 band, codes)."""
+    idx = np.arange(offset, x.shape[0], stride)
     ref, d1, d2, _ = oracle.encode(x[idx], cb)
-    off = oracle.code_offsets(w.n_sub, t_cap)[t_start + idx]  # [n, M]
+    pos = (t_start + idx) if positions is None else np.asarray(positions)[idx]
+    off = oracle.code_offsets(w.n_sub, t_cap)[pos]  # [n, M]
     got = planes[:, off].transpose(1, 0, 2)  # [n, H, M]
     n_amb, n_tot = check_codes(got, x[idx], cb, ref, d1, d2)
-    _log(f"encode parity on {len(idx)} tokens (stride {stride}): {n_amb} of {n_tot} codes in the ambiguity band")
-    return ref
+    n_abs = int(np.sum((d2 - d1) < 1e-5))
+    _log(f"{what} encode parity on {len(idx)} tokens (stride {stride}, offset {offset}): {n_amb} of {n_tot} "
+         f"codes in the relative band, {n_abs} in an absolute 1e-5 band")
+    return ref, n_amb, n_abs, n_tot
 
 
 def _decode_and_check(w, layer, q, cbk, cbv, codes_k, codes_v, hist, rk, rv, rec):
@@ -86,7 +100,7 @@ def test_llama2_7b_32k_full():
         cb = _fitted(w.name, 0, tensor)
         x = synthkv.history_kv(w, 0, tensor, 0)
         planes = _gpu_encode_seq(w, x, cb, w.t_cap)
-        codes[tensor] = _check_sampled_codes(w, x, cb, planes, w.t_cap, stride=1)
+        codes[tensor] = _check_sampled_codes(w, x, cb, planes, w.t_cap, stride=1, what=tensor)[0]
     ck = codes["k"].transpose(1, 0, 2)[None]
     cv = codes["v"].transpose(1, 0, 2)[None]
     _decode_and_check(w, 0, synthkv.queries(w), _fitted(w.name, 0, "k"), _fitted(w.name, 0, "v"), ck, cv,
@@ -94,8 +108,9 @@ def test_llama2_7b_32k_full():
 
 
 def test_batched_16x8k_full():
-    """Batch 16 x 8192: the 16x8192 prefill encoded in one launch (sampled check),
-    decode of all 16 sequences in one call."""
+    """Batch 16 x 8192: the 16x8192 prefill encoded in one launch, every sequence
+    checked on every 8th token (offset rotating with the sequence), and decode of all
+    16 sequences in one call."""
     import torch
 
     import decode_attention_pq_amd as P
@@ -109,8 +124,13 @@ def test_batched_16x8k_full():
         P.encode(_dims(w), to_dev(x), to_dev(cb), planes, w.t_cap)
         torch.cuda.synchronize()
         planes = planes.cpu().numpy()
-        for b in (0, 7, 15):
-            _check_sampled_codes(w, x[b], cb, planes[b], w.t_cap, stride=8)
+        tot = np.zeros(3, np.int64)
+        for b in range(w.batch):
+            _, n_amb, n_abs, n_tot = _check_sampled_codes(w, x[b], cb, planes[b], w.t_cap, stride=8, offset=b % 8,
+                                                          what=f"{tensor} seq {b}")
+            tot += (n_amb, n_abs, n_tot)
+        _log(f"{w.name} {tensor}: {tot[2]} codes checked, {tot[0]} in the relative band, {tot[1]} in an "
+             f"absolute 1e-5 band")
         del x
     ck = synthkv.small_codes(31, (w.batch, H, w.t_cap, M), w.n_centroids)
     cv = synthkv.small_codes(32, (w.batch, H, w.t_cap, M), w.n_centroids)
@@ -126,37 +146,90 @@ def test_gqa_llama3_8b_128k_full():
         cb = _fitted(w.name, 0, tensor)
         x = synthkv.history_kv(w, 0, tensor, 0)
         planes = _gpu_encode_seq(w, x, cb, w.t_cap)
-        codes[tensor] = _check_sampled_codes(w, x, cb, planes, w.t_cap, stride=1)
+        codes[tensor] = _check_sampled_codes(w, x, cb, planes, w.t_cap, stride=1, what=tensor)[0]
         del x
     _decode_and_check(w, 0, synthkv.queries(w), _fitted(w.name, 0, "k"), _fitted(w.name, 0, "v"),
                       codes["k"].transpose(1, 0, 2)[None], codes["v"].transpose(1, 0, 2)[None], w.hist_len,
                       synthkv.recent_kv(w, 0, "k"), synthkv.recent_kv(w, 0, "v"), [w.recent_len] * w.batch)
 
 
-@pytest.mark.parametrize("layer", [0, 31])
-def test_full32_ragged4_layer(layer):
-    """One layer of the ragged 4-sequence workload at full size: the 32768-token
-    prefill encode (sampled check), each sequence's history encoded into its
-    cache slot (sampled check) and decoded with the ragged lengths."""
+def _full32_codebook(w, layer, tensor):
+    """Oracle-fitted codebooks for layers 0 and 31, codebooks drawn from the data
+    distribution for the others (fitting all 64 tensors on the CPU would take an hour)."""
+    if layer in (0, w.n_layers - 1):
+        return _fitted(w.name, layer, tensor)
+    return synthkv.drawn_codebook(w, layer, tensor)
+
+
+LAYER_GROUPS = [list(range(g * 8, g * 8 + 8)) for g in range(4)]
+
+
+@pytest.mark.parametrize("group", range(4))
+def test_full32_ragged4_prefill_encode(group):
+    """The 32768-token prefill of every layer, encoded in one launch per tensor as the
+    benchmark times it; every 8th token checked, from an offset that rotates with the
+    layer."""
+    w = synthkv.WORKLOADS["full32_ragged4"]
+    tot = np.zeros(3, np.int64)
+    for layer in LAYER_GROUPS[group]:
+        for tensor in ("k", "v"):
+            cb = _full32_codebook(w, layer, tensor)
+            x = synthkv.kv_values(w, layer, tensor, "prefill", w.prefill_len)
+            planes = _gpu_encode_seq(w, x, cb, w.prefill_len)
+            _, n_amb, n_abs, n_tot = _check_sampled_codes(w, x, cb, planes, w.prefill_len, stride=8,
+                                                          offset=layer % 8, what=f"layer {layer} {tensor} prefill")
+            tot += (n_amb, n_abs, n_tot)
+            del x
+    _log(f"layers {LAYER_GROUPS[group][0]}-{LAYER_GROUPS[group][-1]} prefill: {tot[2]} codes checked, {tot[0]} in "
+         f"the relative band, {tot[1]} in an absolute 1e-5 band")
+
+
+@pytest.mark.parametrize("group", range(4))
+def test_full32_ragged4_history_encode(group):
+    """Every (layer, sequence) history: a seeded eighth of its 1024-token chunks drawn,
+    each encoded into its place in the sequence's cache plane, every token of them
+    checked (an eighth of all history tokens)."""
     import torch
 
     import decode_attention_pq_amd as P
 
     w = synthkv.WORKLOADS["full32_ragged4"]
     H, M, t_cap = w.n_kv_heads, w.n_sub, w.t_cap
+    tot = np.zeros(3, np.int64)
+    for layer in LAYER_GROUPS[group]:
+        for tensor in ("k", "v"):
+            cb = _full32_codebook(w, layer, tensor)
+            cbd = to_dev(cb)
+            for b in range(w.batch):
+                T = w.hist_len[b]
+                chunks = synthkv.sample_chunks(10000 * layer + 100 * b + (tensor == "v"), T)
+                x = synthkv.history_kv(w, layer, tensor, b, chunks)
+                pos = synthkv.chunk_tokens(chunks, T)
+                plane = torch.zeros((1, H, t_cap * M), dtype=torch.uint8, device="cuda")
+                xd = to_dev(x)
+                i = 0
+                for c in chunks:
+                    n = min(synthkv.CHUNK_TOKENS, T - c * synthkv.CHUNK_TOKENS)
+                    P.encode(_dims(w), xd[i:i + n][None], cbd, plane, t_cap, c * synthkv.CHUNK_TOKENS)
+                    i += n
+                torch.cuda.synchronize()
+                _, n_amb, n_abs, n_tot = _check_sampled_codes(
+                    w, x, cb, plane[0].cpu().numpy(), t_cap, stride=1, positions=pos,
+                    what=f"layer {layer} {tensor} seq {b} chunks {chunks}")
+                tot += (n_amb, n_abs, n_tot)
+                del x, xd, plane
+    _log(f"layers {LAYER_GROUPS[group][0]}-{LAYER_GROUPS[group][-1]} histories: {tot[2]} codes checked, {tot[0]} "
+         f"in the relative band, {tot[1]} in an absolute 1e-5 band")
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_full32_ragged4_layer(layer):
+    """One layer of the ragged 4-sequence workload at full size with its fitted
+    codebooks, decoded with the ragged lengths (its codes' encode parity is covered
+    above)."""
+    w = synthkv.WORKLOADS["full32_ragged4"]
+    H, M, t_cap = w.n_kv_heads, w.n_sub, w.t_cap
     cbs = {t: _fitted(w.name, layer, t) for t in ("k", "v")}
-    for tensor in ("k", "v"):
-        x = synthkv.kv_values(w, layer, tensor, "prefill", w.prefill_len)
-        planes = _gpu_encode_seq(w, x, cbs[tensor], w.prefill_len)
-        _check_sampled_codes(w, x, cbs[tensor], planes, w.prefill_len, stride=16)
-        del x
-        cache = torch.zeros((w.batch, H, t_cap * M), dtype=torch.uint8, device="cuda")
-        for b in range(w.batch):
-            xb = synthkv.history_kv(w, layer, tensor, b)
-            P.encode(_dims(w), to_dev(xb)[None], to_dev(cbs[tensor]), cache[b:b + 1], t_cap)
-            torch.cuda.synchronize()
-            _check_sampled_codes(w, xb, cbs[tensor], cache[b].cpu().numpy(), t_cap, stride=32)
-            del xb
     ck = synthkv.small_codes(100 + layer, (w.batch, H, t_cap, M), w.n_centroids)
     cv = synthkv.small_codes(200 + layer, (w.batch, H, t_cap, M), w.n_centroids)
     _decode_and_check(w, layer, synthkv.queries(w, layer), cbs["k"], cbs["v"], ck, cv, w.hist_len,

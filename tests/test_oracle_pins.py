@@ -181,6 +181,71 @@ def test_encode_pure_python_tiny(oracle_mod):
     assert np.all(amb[:, 1, :][codes[:, 1, :] == 1])  # every pick of the duplicate is ambiguous
 
 
+def _sq_norm_f64(c):
+    """Squared distance of the zero vector to centroid c, summed over j in order in
+    fp64 (each square of an fp32 value is exact in fp64)."""
+    s = 0.0
+    for v in c:
+        t = 0.0 - float(v)
+        s += t * t
+    return s
+
+
+# fp32 values whose squared norm, summed in order in fp64, is exactly fl(1e-5): a runner-up
+# at distance exactly 1e-5 * max(1, 0) from a best at distance 0
+_EXACT_BAND = tuple(np.float32(float.fromhex(h)) for h in
+                    ("0x1.9e772p-9", "0x1.08e4p-15", "0x1.c8d6d4p-20"))
+
+
+def _band_case(best, runner_up):
+    """x = 0 in 4 dimensions (one subspace of d_sub 4) and a codebook whose centroid 0
+    is `best`, centroid 1 `runner_up` and centroids 2, 3 far away."""
+    cb = np.zeros((1, 4, 1, 4), np.float32)
+    cb[0, 0, 0, :len(best)] = best
+    cb[0, 1, 0, :len(runner_up)] = runner_up
+    cb[0, 2, 0, :] = 100.0
+    cb[0, 3, 0, :] = -100.0
+    return np.zeros((1, 1, 4), np.float32), cb
+
+
+def test_encode_ambiguity_band_boundaries(oracle_mod):
+    """The flag is D2 - D1 < 1e-5 * max(1, D1) (strict, relative to the best distance,
+    floored at 1).  Constructed pairs at half and at twice the band for D1 = 0, 0.25, 1
+    and 1000, one at exactly the band, and one just past the band at D1 = 1000 whose
+    runner-up is inside 1e-5 * D2: together they fail an absolute 1e-5 or 1e-4 band, a
+    band without the floor, '<=' for '<', and max(1, D2) for max(1, D1)."""
+    f = np.float32
+    cases = [
+        # (best centroid, runner-up centroid, ambiguous?)
+        ((0.0,), (f(np.sqrt(5e-6)),), True),            # D1 = 0: gap 0.5 band
+        ((0.0,), (f(np.sqrt(2e-5)),), False),           # D1 = 0: gap 2 bands
+        ((0.5,), (0.5, f(np.sqrt(5e-6))), True),        # D1 = 0.25: band 1e-5 (floor), gap 5e-6
+        ((0.5,), (0.5, f(np.sqrt(2e-5))), False),       # D1 = 0.25: gap 2e-5 (inside a 1e-4 band)
+        ((1.0,), (1.0, f(np.sqrt(5e-6))), True),        # D1 = 1
+        ((1.0,), (1.0, f(np.sqrt(2e-5))), False),
+        ((30.0, 10.0), (30.0, 10.0, f(np.sqrt(5e-3))), True),   # D1 = 1000: band 1e-2, gap 5e-3
+        ((30.0, 10.0), (30.0, 10.0, f(np.sqrt(2e-2))), False),  # D1 = 1000: gap 2e-2
+        ((0.0,), _EXACT_BAND, False),                   # D1 = 0, gap exactly fl(1e-5): '<' says no
+        ((30.0, 10.0), (30.0, 10.0, f(0.1)), False),    # gap 1e-2 + 3e-10: past 1e-5 * D1, inside 1e-5 * D2
+    ]
+    assert _sq_norm_f64(_EXACT_BAND) == 1e-5
+    for best, runner, want in cases:
+        x, cb = _band_case(best, runner)
+        codes, d1, d2, amb = oracle.encode(x, cb)
+        e1, e2 = _sq_norm_f64(cb[0, 0, 0]), _sq_norm_f64(cb[0, 1, 0])
+        assert codes[0, 0, 0] == 0 and d1[0, 0, 0] == e1 and d2[0, 0, 0] == e2, (best, runner)
+        assert bool(amb[0, 0, 0]) == want, (best, runner, e1, e2)
+        # the same pair with the two centroids swapped: the code follows the best one
+        cb2 = cb[:, [1, 0, 2, 3]].copy()
+        codes2, d1b, d2b, amb2 = oracle.encode(x, cb2)
+        assert codes2[0, 0, 0] == 1 and d1b[0, 0, 0] == e1 and bool(amb2[0, 0, 0]) == want
+    # the band boundaries the mistaken readings would give, on the same pairs
+    b0 = _sq_norm_f64(_EXACT_BAND)
+    assert not (b0 - 0.0 < 1e-5 * max(1.0, 0.0)) and (b0 - 0.0 <= 1e-5 * max(1.0, 0.0))
+    e1, e2 = 1000.0, _sq_norm_f64((30.0, 10.0, f(0.1)))
+    assert not (e2 - e1 < 1e-5 * max(1.0, e1)) and (e2 - e1 < 1e-5 * max(1.0, e2))
+
+
 def test_encode_matches_scipy_vq(oracle_mod):
     """Library pin: scipy's vector quantiser (nearest code by Euclidean distance)."""
     from scipy.cluster.vq import vq
@@ -479,6 +544,20 @@ def test_generator_deterministic_and_shaped():
     assert synthkv.WORKLOADS["full32_ragged4"].hist_len == (14698, 3634, 31436, 30564)
     v = synthkv.kv_values(w, 0, "v", "history", 256)
     assert not np.array_equal(a, v)
+
+
+def test_generator_chunks_draw_alone():
+    """A sample of 1024-token chunks, drawn alone, equals the same tokens of the whole
+    draw (ragged last chunk included); the sample is seeded and 1/8 of the chunks."""
+    w = synthkv.WORKLOADS["full32_ragged4"]
+    n = 5000
+    full = synthkv.kv_values(w, 3, "v", "history", n, 1)
+    part = synthkv.kv_values(w, 3, "v", "history", n, 1, chunks=[1, 4])
+    np.testing.assert_array_equal(part, full[synthkv.chunk_tokens([1, 4], n)])
+    assert part.shape[0] == 1024 + (n - 4096)
+    ch = synthkv.sample_chunks(11, 31436)
+    assert ch == synthkv.sample_chunks(11, 31436) and len(ch) == 4 and ch == sorted(set(ch))
+    assert len(synthkv.sample_chunks(11, 1000)) == 1
 
 
 # ------------------------------------------------------------------ O7 live-cache step
