@@ -15,7 +15,7 @@ import torch  # loads the HIP runtime libpqkv.so binds to (same soname)
 
 __all__ = [
     "PQKVError", "Dims", "lib", "LIB_PATH", "encode", "build_lut", "decode_workspace_bytes",
-    "decode_attention", "append_kv", "fit_codebooks", "merge", "code_plane_bytes", "MAX_FIT_POINTS", "F16", "F32", "MAX_RECENT", "TILE_TOKENS",
+    "decode_attention", "append_kv", "NOALLOC_SCRATCH_BYTES", "NOALLOC_MAX_ROWS", "fit_codebooks", "merge", "code_plane_bytes", "MAX_FIT_POINTS", "F16", "F32", "MAX_RECENT", "TILE_TOKENS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpqkv.so")
@@ -23,6 +23,8 @@ F16, F32 = 0, 1
 MAX_RECENT = 1024
 MAX_FIT_POINTS = 8192
 TILE_TOKENS = 64
+NOALLOC_SCRATCH_BYTES = 8 << 20
+NOALLOC_MAX_ROWS = 16384
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace missing or too small",
            4: "HIP launch failed"}
@@ -68,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.pqkv_decode_attention.argtypes = [dp, i32, vp, i32, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp, i32,
                                             i64, vp, f32, vp, vp, vp, sz, vp]
         L.pqkv_decode_attention.restype = i32
+        L.pqkv_decode_attention_noalloc.argtypes = [dp, i32, vp, i32, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp,
+                                                    i32, i64, vp, f32, vp, vp, vp]
+        L.pqkv_decode_attention_noalloc.restype = i32
         L.pqkv_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                      i64, i64, vp]
         L.pqkv_append_kv.restype = i32
@@ -156,12 +161,13 @@ def _check_numel(name, t, n):
 
 def decode_attention(dims: Dims, q, codebook_k, codebook_v, codes_k, codes_v, t_cap: int, hist_len,
                      max_hist_len: int, recent_k, recent_v, recent_len, softmax_scale: float, out, lse,
-                     workspace, lut=None) -> None:
+                     workspace, lut=None, noalloc=False) -> None:
     """pqkv_decode_attention.  q: [B, Hq, d]; codes_k/v: uint8 [B, Hkv, t_cap*M];
     hist_len/recent_len: int32 [B] (device); recent_k/v: [B, Hkv, r_cap, d] or None;
     out: fp32 [B, Hq, d]; lse: fp32 [B, Hq]; workspace: a device tensor (uint8) or None;
     lut: None (the kernel builds the ad-LUT) or fp32 [B, Hq, M, K] from build_lut
-    (codebook_k may then be None)."""
+    (codebook_k may then be None).  noalloc=True calls pqkv_decode_attention_noalloc
+    (the library's static device array instead of `workspace`, which must be None)."""
     _dev(q, lut, codebook_k, codebook_v, codes_k, codes_v, hist_len, recent_k, recent_v, recent_len, out, lse,
          workspace)
     B = q.shape[0]
@@ -202,6 +208,14 @@ def decode_attention(dims: Dims, q, codebook_k, codebook_v, codes_k, codes_v, t_
         if tuple(recent_k.shape) != (B, Hkv, r_cap, d):
             raise ValueError(f"recent_k has shape {tuple(recent_k.shape)}, expected ({B}, {Hkv}, r_cap, {d})")
         _check_numel("recent_len", recent_len, B)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        _check("pqkv_decode_attention_noalloc", lib().pqkv_decode_attention_noalloc(
+            ctypes.byref(dims), B, _ptr(q), _dtype_code(q), _ptr(lut), _ptr(codebook_k), _ptr(codebook_v),
+            _ptr(codes_k), _ptr(codes_v), t_cap, _ptr(hist_len), max_hist_len, _ptr(recent_k), _ptr(recent_v),
+            rdt, r_cap, _ptr(recent_len), float(softmax_scale), _ptr(out), _ptr(lse), _stream()))
+        return
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pqkv_decode_attention", lib().pqkv_decode_attention(
         ctypes.byref(dims), B, _ptr(q), _dtype_code(q), _ptr(lut), _ptr(codebook_k), _ptr(codebook_v),

@@ -21,7 +21,8 @@
  *     PQKV_ERR_WORKSPACE and enqueues nothing.  A failed launch returns
  *     PQKV_ERR_HIP.  A device-side fault shows up at the caller's next
  *     synchronisation.  No C++ exception crosses this interface.
- *   - The library keeps no mutable global state; calls are thread-safe.
+ *   - The library keeps no mutable global state and its calls are thread-safe,
+ *     except pqkv_decode_attention_noalloc (a static device array per GPU).
  *
  * Shapes and symbols
  *   d = head_dim in {64, 128};  d_sub in {2, 4};  M = d / d_sub subspaces;
@@ -189,6 +190,34 @@ pqkv_status pqkv_decode_attention(const pqkv_dims* dims, int32_t batch, const vo
                                   const int32_t* recent_len, float softmax_scale, float* out,
                                   float* lse, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
+
+/*
+ * pqkv_decode_attention_noalloc -- pqkv_decode_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, same kernels and the same
+ * result, without the workspace: the per-split partials and completion counters
+ * live in a static device array of PQKV_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends.  The first call on a device
+ * looks the array up and clears its counters on `stream` (a small kernel); later
+ * calls allocate nothing and launch only the decode kernel.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (different streams, or host threads) race and give wrong results.  Order them
+ * on one stream.  This entry point keeps global state, unlike the rest of the library.
+ * Errors as for pqkv_decode_attention, and WORKSPACE when batch * n_q_heads exceeds
+ * PQKV_NOALLOC_MAX_ROWS or the partials exceed the array (about 15,000 (sequence,
+ * query head, split) records at head_dim 128).
+ */
+#define PQKV_NOALLOC_SCRATCH_BYTES (8u << 20)
+#define PQKV_NOALLOC_MAX_ROWS 16384
+pqkv_status pqkv_decode_attention_noalloc(const pqkv_dims* dims, int32_t batch, const void* q,
+                                          pqkv_dtype q_dtype, const float* lut, const float* codebook_k,
+                                          const float* codebook_v, const uint8_t* codes_k,
+                                          const uint8_t* codes_v, int64_t t_cap, const int32_t* hist_len,
+                                          int64_t max_hist_len, const void* recent_k, const void* recent_v,
+                                          pqkv_dtype recent_dtype, int64_t r_cap,
+                                          const int32_t* recent_len, float softmax_scale, float* out,
+                                          float* lse, hipStream_t stream);
 
 /*
  * pqkv_append_kv -- one decode step of the live cache: each sequence's new key

@@ -138,6 +138,23 @@ def test_split_plan_choices(P):
                                    5000000, FAKE, FAKE, 0, 0, FAKE, 0.088, FAKE, FAKE, FAKE, need, None) == 2
 
 
+def test_noalloc_refuses_sizes_beyond_its_array(P):
+    """pqkv_decode_attention_noalloc checks on the host that the call fits its static
+    array (rows of counters, then partials) before it touches a device."""
+    L = P.lib()
+
+    def call(batch, hq, maxh, t_cap):
+        return L.pqkv_decode_attention_noalloc(_d(P, 128, 2, 256, hq, hq), batch, FAKE, 0, None, FAKE, FAKE, FAKE,
+                                               FAKE, t_cap, FAKE, maxh, None, None, 0, 0, None, 0.088, FAKE, FAKE,
+                                               None)
+
+    assert P.NOALLOC_MAX_ROWS == 16384 and P.NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert call(600, 32, 64, 64) == 3              # 19200 (sequence, query head) rows
+    assert call(128, 32, 32768, 32768) == 3        # 4 splits each: 8.65 MB of partials
+    assert call(1, 32, 40000, 32768) == 1          # ordinary validation comes first
+    assert call(0, 32, 64, 64) == 0                # nothing to do
+
+
 def test_merge_validation(P):
     L = P.lib()
     assert L.pqkv_merge(-1, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
