@@ -51,9 +51,7 @@ def parse():
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-COUNTERS = os.path.join(ROOT, "profiles", "pq_decode_kernel__llama2_7b_32k.counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_pq_amd", "csrc", f)
-                  for f in ("decode_kernel.h", "decode_m64d2.hip", "decode_plan.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_pq_amd", "csrc", f) for f in ("decode_kernel.h", "decode_plan.h")]
 
 
 def kernel_source_hash() -> str:
@@ -70,7 +68,7 @@ def measured_traffic(workload: str):
     """HBM bytes per decode dispatch from the committed rocprofv3 counter runs,
     or None if they were taken on another workload or another kernel source."""
     try:
-        with open(COUNTERS) as f:
+        with open(os.path.join(ROOT, "profiles", f"pq_decode_kernel__{workload}.counters.json")) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
