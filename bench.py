@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--encode-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
+    ap.add_argument("--no-fp16", action="store_true", help="skip the dense fp16 decode baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU work for the baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates the HBM byte counters)")
@@ -263,6 +264,40 @@ def main():
     per_call_us = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 / calls_per_step for i in range(nper))
     pct = lambda p: round(per_call_us[min(len(per_call_us) - 1, int(p * len(per_call_us)))], 3)
 
+    # the dense fp16 baseline (pqkv_fp16_decode_attention) at the same shape: history and recent
+    # window as one fp16 cache, rotated over two copies (>= 1 GiB for the 32K and 128K shapes)
+    fp16 = None
+    if calls_per_step == 1 and not args.no_fp16:
+        n_ctx = T + R
+        f_cap = -(-n_ctx // 64) * 64
+        fk = [torch.randn((B, Hkv, f_cap, d), device=dev, dtype=torch.float16) for _ in range(2)]
+        fv = [torch.randn((B, Hkv, f_cap, d), device=dev, dtype=torch.float16) for _ in range(2)]
+        flen = torch.full((B,), n_ctx, dtype=torch.int32, device=dev)
+        fws = torch.zeros(P.fp16_decode_workspace_bytes(dims, B, n_ctx), dtype=torch.uint8, device=dev)
+        fq = copies[0]["q"].to(torch.float16)
+
+        def fcall(i):
+            P.fp16_decode_attention(dims, fq, fk[i % 2], fv[i % 2], f_cap, flen, n_ctx, scale, out, lse, fws)
+
+        for i in range(args.warmup):
+            fcall(i)
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for i in range(args.steps):
+            fcall(i)
+        f1.record()
+        torch.cuda.synchronize()
+        f_us = f0.elapsed_time(f1) * 1e3 / args.steps
+        f_bytes = 2 * 2 * d * n_ctx * B * Hkv + 2 * d * B * Hq + (4 * d + 4) * B * Hq
+        fp16 = {"kernel": "fp16_decode_kernel (pqkv_fp16_decode_attention)", "us_per_call": round(f_us, 3),
+                "bytes_per_call": f_bytes, "gbs": round(f_bytes / (f_us * 1e-6) / 1e9, 1),
+                "frac": round(f_bytes / (f_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "pq_speedup": round(f_us / (ms * 1e3), 3),
+                "page_figure": "about 2x lower time per output token than an FP16 cache at 32K context "
+                               "(end to end, whole model; hardware not stated): context only"}
+        del fk, fv, fws
+
     # the product path on given inputs, for the CPU leg's parity check (outside the timed region)
     def gpu_decode_one(q, cb_k, cb_v, planes_k, planes_v, T0, rk0, rv0, R0):
         """One pqkv_decode_attention call of one sequence: numpy in (code planes in the
@@ -386,6 +421,8 @@ def main():
     }
     if fit is not None:
         result["fit_codebooks"] = fit
+    if fp16 is not None:
+        result["fp16_baseline"] = fp16
     if append_us is not None:
         result["append_kv_us"] = append_us
     for c in copies:

@@ -15,7 +15,7 @@ import torch  # loads the HIP runtime libpqkv.so binds to (same soname)
 
 __all__ = [
     "PQKVError", "Dims", "lib", "LIB_PATH", "encode", "build_lut", "decode_workspace_bytes",
-    "decode_attention", "append_kv", "NOALLOC_SCRATCH_BYTES", "NOALLOC_MAX_ROWS", "fit_codebooks", "merge", "code_plane_bytes", "MAX_FIT_POINTS", "F16", "F32", "MAX_RECENT", "TILE_TOKENS",
+    "decode_attention", "fp16_decode_workspace_bytes", "fp16_decode_attention", "append_kv", "NOALLOC_SCRATCH_BYTES", "NOALLOC_MAX_ROWS", "fit_codebooks", "merge", "code_plane_bytes", "MAX_FIT_POINTS", "F16", "F32", "MAX_RECENT", "TILE_TOKENS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpqkv.so")
@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.pqkv_decode_attention_noalloc.argtypes = [dp, i32, vp, i32, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp,
                                                     i32, i64, vp, f32, vp, vp, vp]
         L.pqkv_decode_attention_noalloc.restype = i32
+        L.pqkv_fp16_decode_workspace_bytes.argtypes = [dp, i32, i64]
+        L.pqkv_fp16_decode_workspace_bytes.restype = sz
+        L.pqkv_fp16_decode_attention.argtypes = [dp, i32, vp, vp, vp, i64, vp, i64, f32, vp, vp, vp, sz, vp]
+        L.pqkv_fp16_decode_attention.restype = i32
         L.pqkv_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                      i64, i64, vp]
         L.pqkv_append_kv.restype = i32
@@ -222,6 +226,37 @@ def decode_attention(dims: Dims, q, codebook_k, codebook_v, codes_k, codes_v, t_
         _ptr(codes_k), _ptr(codes_v), t_cap, _ptr(hist_len), max_hist_len, _ptr(recent_k), _ptr(recent_v), rdt,
         r_cap, _ptr(recent_len), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
         _stream()))
+
+
+def fp16_decode_workspace_bytes(dims: Dims, batch: int, max_len: int) -> int:
+    return int(lib().pqkv_fp16_decode_workspace_bytes(ctypes.byref(dims), batch, max_len))
+
+
+def fp16_decode_attention(dims: Dims, q, k_cache, v_cache, t_cap: int, seq_len, max_len: int, softmax_scale: float,
+                          out, lse, workspace) -> None:
+    """pqkv_fp16_decode_attention (the dense fp16 baseline).  q: fp16 [B, Hq, d];
+    k_cache/v_cache: fp16 [B, Hkv, t_cap, d]; seq_len: int32 [B] (device);
+    out: fp32 [B, Hq, d]; lse: fp32 [B, Hq]; workspace: a device tensor (uint8)."""
+    _dev(q, k_cache, v_cache, seq_len, out, lse, workspace)
+    B = q.shape[0]
+    d, Hq, Hkv = dims.head_dim, dims.n_q_heads, dims.n_kv_heads
+    for t in (q, k_cache, v_cache, seq_len, out, lse):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if q.dtype != torch.float16 or k_cache.dtype != torch.float16 or v_cache.dtype != torch.float16:
+        raise ValueError("q and the caches must be fp16")
+    if seq_len.dtype != torch.int32 or out.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise ValueError("seq_len must be int32, out and lse fp32")
+    _check_numel("q", q, B * Hq * d)
+    _check_numel("k_cache", k_cache, B * Hkv * t_cap * d)
+    _check_numel("v_cache", v_cache, B * Hkv * t_cap * d)
+    _check_numel("seq_len", seq_len, B)
+    _check_numel("out", out, B * Hq * d)
+    _check_numel("lse", lse, B * Hq)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pqkv_fp16_decode_attention", lib().pqkv_fp16_decode_attention(
+        ctypes.byref(dims), B, _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, _ptr(seq_len), max_len,
+        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream()))
 
 
 def append_kv(dims: Dims, new_k, new_v, recent_k, recent_v, hist_len_in, recent_len_in, hist_len_out,

@@ -166,6 +166,43 @@ DecodeArgs decode_args(const void* q, const float* lut, const float* codebook_k,
     return a;
 }
 
+Fp16Plan plan_fp16_decode(int head_dim, int n_q_heads, int n_kv_heads, int32_t batch, int64_t max_len) {
+    // About two work-groups per CU (each holds 16 KiB of loads in flight per wave),
+    // splits of a multiple of 128 tokens (a round of the 4 waves at d = 128), at most 64.
+    Fp16Plan p{};
+    const int64_t units = (int64_t)batch * n_kv_heads;
+    const int64_t want = units > 0 ? (2 * kPlanCUs + units - 1) / units : 1;
+    int64_t ns = want < 1 ? 1 : (want > 64 ? 64 : want);
+    if (max_len <= 0) {
+        ns = 1;
+        p.split_tokens = 128;
+    } else {
+        const int64_t most = (max_len + 511) / 512;  // splits of at least 512 tokens
+        ns = ns > most ? most : ns;
+        p.split_tokens = ((max_len + ns - 1) / ns + 127) / 128 * 128;
+        ns = (max_len + p.split_tokens - 1) / p.split_tokens;
+    }
+    p.n_split = (int)ns;
+    p.partial_stride = head_dim + 4;
+    p.partials_offset = decode_counter_bytes(batch, n_q_heads);
+    const size_t part = (size_t)batch * n_q_heads * p.n_split * p.partial_stride * sizeof(float);
+    p.workspace_bytes = p.partials_offset + (part + 255) / 256 * 256;
+    return p;
+}
+
+namespace {
+
+pqkv_status check_fp16_dims(const pqkv_dims* d) {
+    if (!d || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1) return PQKV_ERR_INVALID;
+    if (d->n_q_heads % d->n_kv_heads) return PQKV_ERR_INVALID;
+    const int g = d->n_q_heads / d->n_kv_heads;
+    if ((d->head_dim != 64 && d->head_dim != 128) || (g != 1 && g != 2 && g != 4 && g != 8)) return PQKV_ERR_UNSUPPORTED;
+    if (d->n_kv_heads > 65535) return PQKV_ERR_UNSUPPORTED;
+    return PQKV_OK;
+}
+
+}  // namespace
+
 }  // namespace pqkv
 
 using namespace pqkv;
@@ -244,6 +281,44 @@ pqkv_status pqkv_decode_attention(const pqkv_dims* dims, int32_t batch, const vo
                                      static_cast<uint32_t*>(workspace),
                                      reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.partials_offset));
     return hip_status(launch_decode(*dims, batch, q_dtype, recent_dtype, plan, a, stream));
+}
+
+size_t pqkv_fp16_decode_workspace_bytes(const pqkv_dims* dims, int32_t batch, int64_t max_len) {
+    if (check_fp16_dims(dims) != PQKV_OK || batch <= 0 || max_len < 0) return 0;
+    return plan_fp16_decode(dims->head_dim, dims->n_q_heads, dims->n_kv_heads, batch, max_len).workspace_bytes;
+}
+
+pqkv_status pqkv_fp16_decode_attention(const pqkv_dims* dims, int32_t batch, const void* q, const void* k_cache,
+                                       const void* v_cache, int64_t t_cap, const int32_t* seq_len, int64_t max_len,
+                                       float softmax_scale, float* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    const pqkv_status ds = check_fp16_dims(dims);
+    if (ds != PQKV_OK) return ds;
+    if (batch < 0 || max_len < 0 || t_cap < 0 || max_len > t_cap) return PQKV_ERR_INVALID;
+    if (batch == 0) return PQKV_OK;
+    if (!q || !k_cache || !v_cache || !seq_len || !out || !lse) return PQKV_ERR_INVALID;
+    // rows are read 16 bytes per lane
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return PQKV_ERR_INVALID;
+    if (!(softmax_scale == softmax_scale)) return PQKV_ERR_INVALID;
+    if ((int64_t)batch * dims->n_kv_heads * 64 > 0x7fffffffLL) return PQKV_ERR_UNSUPPORTED;
+    const Fp16Plan plan = plan_fp16_decode(dims->head_dim, dims->n_q_heads, dims->n_kv_heads, batch, max_len);
+    if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned(workspace, 256)) return PQKV_ERR_WORKSPACE;
+    Fp16Call c;
+    c.head_dim = dims->head_dim;
+    c.n_q_heads = dims->n_q_heads;
+    c.n_kv_heads = dims->n_kv_heads;
+    c.q = q;
+    c.k = k_cache;
+    c.v = v_cache;
+    c.t_cap = t_cap;
+    c.seq_len = seq_len;
+    c.max_len = max_len;
+    c.scale = softmax_scale;
+    c.out = out;
+    c.lse = lse;
+    c.counters = static_cast<uint32_t*>(workspace);
+    c.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.partials_offset);
+    return hip_status(launch_fp16_decode(plan, batch, c, stream));
 }
 
 pqkv_status pqkv_merge(int64_t n_rows, int32_t head_dim, const float* out_a, const float* lse_a,

@@ -29,6 +29,36 @@ hipError_t launch_kmeans(const pqkv_dims& d, const void* x, pqkv_dtype xt, int64
                          int64_t s_head, const int32_t* order, int32_t iters, float* cb, int32_t* kept,
                          hipStream_t stream);
 
+// Dense fp16 decode attention (the full-precision baseline).
+constexpr int kFp16Threads = 256;  // 4 waves per work-group
+
+struct Fp16Plan {
+    int n_split;           // token splits per (sequence, kv head)
+    int64_t split_tokens;  // tokens per split (a multiple of 128)
+    int partial_stride;    // floats per partial record: d outputs + max + sum, padded
+    size_t partials_offset;
+    size_t workspace_bytes;
+};
+
+struct Fp16Call {
+    int head_dim, n_q_heads, n_kv_heads;
+    const void* q;  // fp16 [B][Hq][d]
+    const void* k;  // fp16 [B][Hkv][t_cap][d]
+    const void* v;
+    int64_t t_cap;
+    const int32_t* seq_len;  // device [B]
+    int64_t max_len;
+    float scale;
+    float* out;
+    float* lse;
+    float* partials;
+    uint32_t* counters;
+};
+
+Fp16Plan plan_fp16_decode(int head_dim, int n_q_heads, int n_kv_heads, int32_t batch, int64_t max_len);
+
+hipError_t launch_fp16_decode(const Fp16Plan& p, int32_t batch, const Fp16Call& c, hipStream_t stream);
+
 hipError_t launch_merge_states(int64_t n_rows, int32_t head_dim, const float* out_a,
                                const float* lse_a, const float* out_b, const float* lse_b,
                                float* out, float* lse, hipStream_t stream);

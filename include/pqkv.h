@@ -220,6 +220,34 @@ pqkv_status pqkv_decode_attention_noalloc(const pqkv_dims* dims, int32_t batch, 
                                           float* lse, hipStream_t stream);
 
 /*
+ * pqkv_fp16_decode_attention -- dense fp16 decode attention over a full-precision
+ * K/V cache: the baseline the page compares MILLION's decode speed with (Fig. 12
+ * paragraph: time per output token against an FP16 KV cache).  It computes the
+ * same softmax attention as pqkv_decode_attention's definition, with every cached
+ * token's key and value read from the fp16 cache:
+ *     s_i = softmax_scale * q . k_i,  out = sum_i exp(s_i - mu) v_i / sum_i exp(s_i - mu),
+ *     lse = mu + ln sum_i exp(s_i - mu),   i < seq_len[b];  no tokens: out = 0, lse = -inf.
+ * Split-K over tokens (flash decoding) with fp32 accumulation.
+ *
+ *   dims          head_dim (64 or 128), n_q_heads, n_kv_heads (Hq / Hkv in {1, 2, 4, 8});
+ *                 d_sub and n_centroids are not read.
+ *   q             device fp16 [batch][Hq][d], 16-byte aligned.
+ *   k_cache/v_cache  device fp16 [batch][Hkv][t_cap][d], 16-byte aligned.
+ *   seq_len       device int32 [batch], each in [0, max_len] (clamped to it).
+ *   max_len       host bound on seq_len, <= t_cap.
+ *   out, lse      device fp32 [batch][Hq][d] and [batch][Hq].
+ *   workspace     as for pqkv_decode_attention (counters first, zeroed before first use),
+ *                 >= pqkv_fp16_decode_workspace_bytes(dims, batch, max_len) bytes.
+ * Errors: INVALID for null or misaligned pointers, negative sizes, max_len > t_cap;
+ * UNSUPPORTED for other head sizes or group sizes; WORKSPACE for a short workspace.
+ */
+size_t pqkv_fp16_decode_workspace_bytes(const pqkv_dims* dims, int32_t batch, int64_t max_len);
+pqkv_status pqkv_fp16_decode_attention(const pqkv_dims* dims, int32_t batch, const void* q, const void* k_cache,
+                                       const void* v_cache, int64_t t_cap, const int32_t* seq_len, int64_t max_len,
+                                       float softmax_scale, float* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pqkv_append_kv -- one decode step of the live cache: each sequence's new key
  * and value enter its recent full-precision window, and a window that is full
  * first rolls its oldest n_roll tokens into the PQ history.  This is the batched,
