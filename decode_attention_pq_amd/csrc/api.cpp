@@ -85,7 +85,8 @@ DecodePlan plan_decode(const pqkv_dims& d, int32_t batch, int64_t max_hist_len) 
             if (ns > kMaxSplits && (n_split != 0 || r < decode_max_rounds(M, qh))) continue;
             const int64_t items = p.units * ns;
             const int64_t waves = (items + kPlanCUs - 1) / kPlanCUs;
-            const int64_t cost = waves * (48 + 20 * rr + 3 * (decode_kernel_rounds(M, qh, (int)rr) - rr));
+            const int64_t cost =
+                waves * (kPlanFixed + kPlanRound * rr + kPlanUnused * (decode_kernel_rounds(M, qh, (int)rr) - rr));
             if (n_split == 0 || cost < best_cost || (cost == best_cost && items < best_items)) {
                 n_split = ns;
                 rounds = rr;

@@ -103,6 +103,24 @@ __device__ inline uint32_t wave_sum_u32(uint32_t v) {
     return wave_reduce(v, 0u, [](uint32_t x, uint32_t y) { return x + y; });
 }
 
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+    return wave_reduce(v, 0xffffffffu, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+}
+
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+    return wave_reduce(v, 0u, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+}
+
+// ceil(x / y) for x, y < 2^22 (x a count of 512-token rounds): a float quotient,
+// corrected to the exact one.
+__device__ inline uint32_t ceil_div_small(uint32_t x, uint32_t y) {
+    uint32_t q = (uint32_t)((float)x / (float)y);
+    q += q * y < x ? 1u : 0u;
+    q += q * y < x ? 1u : 0u;
+    q -= (q > 0u && (q - 1u) * y >= x) ? 1u : 0u;
+    return q;
+}
+
 // LDS byte offset of a pointer into a __shared__ array.
 __device__ inline uint32_t lds_offset(const float* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)p;
@@ -228,7 +246,8 @@ struct DecArgs {
     // first 64 bytes: everything the work mapping and the first loads need, so one
     // scalar load brings it in
     int K, Hq, Hkv, n_groups, n_split, rounds, n_items;
-    int len_first;  // read the lengths before anything else (batches whose lengths may differ)
+    int len_first;  // 0: lengths read after the first loads (one sequence); 1: before them;
+                    // 2: all of them before anything else, for the device-side split plan
     int64_t split_tokens;
     const int32_t* hist_len;
     const int32_t* recent_len;
@@ -295,14 +314,90 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     // every XCD gets a share of every sequence even when their lengths differ.
     const int L = blockIdx.x;
     const int xcd = L & 7;
-    const int item = xcd * (a.n_items >> 3) + (xcd < (a.n_items & 7) ? xcd : (a.n_items & 7)) + (L >> 3);
-    const int unit = item / a.n_split;
-    const int split = item - unit * a.n_split;
-    const int grp = unit % a.n_groups;
-    const int hb = unit / a.n_groups;
+    int item = xcd * (a.n_items >> 3) + (xcd < (a.n_items & 7) ? xcd : (a.n_items & 7)) + (L >> 3);
     const int batch = a.n_items / (a.Hkv * a.n_groups * a.n_split);
-    const int b = hb % batch;
-    const int h = hb / batch;
+    // This work-group's piece: sequence b, kv head h, query-head group grp, split
+    // `split` of the sequence's ns_dev splits (device plan) starting at token t0 and at
+    // most tspan long; its partial record is item item_first + split.
+    int b, h, grp, split, item_first, ns_dev = 0, T_dev = 0;
+    int64_t t0, tspan;
+    int mode = a.len_first;
+    int Tl = 0;
+    if (mode == 2) {
+        // lane l holds sequence l's length; equal lengths keep the host's plan
+        int li = lane < batch ? lane : 0;
+        asm volatile("" : "+v"(li));
+        Tl = a.hist_len[li];
+        Tl = lane < batch ? (Tl < 0 ? 0 : (Tl > (int)a.max_hist ? (int)a.max_hist : Tl)) : 0;
+        const uint32_t lo = wave_min_u32(lane < batch ? (uint32_t)Tl : 0xffffffffu);
+        if (lo == wave_max_u32((uint32_t)Tl)) mode = 1;
+    }
+    if (mode == 2) {
+        // ---- the device-side split plan (2 <= batch <= 16): lane l holds sequence l's
+        // length; lane r - 1 prices splits of at most r rounds (r <= RW, this build) with
+        // the host plan's cost model, over the grid the host launched; the cheapest wins,
+        // fewer work-groups on a tie.  Every wave computes the same plan.
+        const uint32_t u = ((uint32_t)Tl + kTokensPerRound - 1u) / kTokensPerRound;  // rounds of the sequence
+        const uint32_t r = (uint32_t)lane + 1u;
+        uint32_t S = 0u, RRm = 0u;
+        for (int q = 0; q < batch; ++q) {
+            const uint32_t uq = (uint32_t)__builtin_amdgcn_readlane((int)u, q);
+            const uint32_t nb = uq ? ceil_div_small(uq, r) : 1u;
+            const uint32_t rr = uq ? ceil_div_small(uq, nb) : 0u;
+            S += nb;
+            RRm = rr > RRm ? rr : RRm;
+        }
+        const uint64_t items_r = (uint64_t)(a.Hkv * a.n_groups) * S;
+        const uint64_t waves_r = (items_r + kPlanCUs - 1) / kPlanCUs;
+        const uint64_t cost_r = waves_r * (uint64_t)(kPlanFixed + kPlanRound * RRm + kPlanUnused * (RW - RRm));
+        const bool cand = r <= (uint32_t)RW && items_r <= (uint64_t)a.n_items;
+        const uint32_t cost = cand ? (uint32_t)(cost_r < 0xfffffffeull ? cost_r : 0xfffffffeull) : 0xffffffffu;
+        const uint32_t best = wave_min_u32(cost);
+        const uint32_t rbest = wave_max_u32(cost == best ? r : 0u);  // the longest splits among the cheapest
+        const uint32_t nbl = lane < batch ? (u ? ceil_div_small(u, rbest) : 1u) : 0u;
+        const uint32_t Sb = wave_sum_u32(nbl);
+        // the plan's items spread over every XCD the same way, contiguous within one:
+        // XCD x takes ceil((used - x) / 8) of them; the grid's other work-groups exit
+        // (nothing issued yet but the lengths, which have landed)
+        const int used = a.Hkv * a.n_groups * (int)Sb;
+        const int slot = L >> 3;
+        if (slot >= (used - xcd + 7) / 8) return;
+        item = xcd * (used >> 3) + (xcd < (used & 7) ? xcd : (used & 7)) + slot;
+        const int hg = item / (int)Sb;
+        const int kk = item - hg * (int)Sb;
+        int acc = 0, bq = 0;
+        for (int q = 0; q < batch; ++q) {
+            const int n = __builtin_amdgcn_readlane((int)nbl, q);
+            if (kk < acc + n) {
+                bq = q;
+                break;
+            }
+            acc += n;
+        }
+        b = bq;
+        split = kk - acc;
+        ns_dev = __builtin_amdgcn_readlane((int)nbl, b);
+        T_dev = __builtin_amdgcn_readlane(Tl, b);
+        // even splits of the sequence, whole 64-token tiles each
+        tspan = T_dev > 0 ? ((int64_t)(((uint32_t)T_dev + (uint32_t)ns_dev - 1u) / (uint32_t)ns_dev) + kTileTokens - 1) /
+                                kTileTokens * kTileTokens
+                          : kTileTokens;
+        t0 = (int64_t)split * tspan;
+        grp = hg % a.n_groups;
+        h = hg / a.n_groups;
+        item_first = hg * (int)Sb + acc;
+    } else {
+        const int unit0 = item / a.n_split;
+        split = item - unit0 * a.n_split;
+        grp = unit0 % a.n_groups;
+        const int hb = unit0 / a.n_groups;
+        b = hb % batch;
+        h = hb / batch;
+        item_first = unit0 * a.n_split;
+        t0 = (int64_t)split * a.split_tokens;
+        tspan = a.split_tokens;
+    }
+    const int unit = (h * batch + b) * a.n_groups + grp;  // its completion counter
     const int hq0 = h * (a.Hq / a.Hkv) + grp * QH;
     const int K = a.K;
 
@@ -311,9 +406,9 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     // are used only after the length-independent loads below have been issued.
     int len_idx = b;
     asm volatile("" : "+v"(len_idx));  // a per-lane index makes these vector loads
-    const int T_in = a.hist_len ? a.hist_len[len_idx] : 0;  // no history: no lengths either
+    // (the device plan has read every length already)
+    const int T_in = mode == 2 ? T_dev : (a.hist_len ? a.hist_len[len_idx] : 0);  // no history: no lengths
     const int R_in = a.recent_len ? a.recent_len[len_idx] : 0;
-    const int64_t t0 = (int64_t)split * a.split_tokens;
     // A sequence uses the splits that hold its history (at least one, which also
     // takes the recent window or gives the empty result); work-groups of the other
     // splits have nothing to do.  When lengths may differ, they learn it before
@@ -323,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         return Tc > 0 ? (int)(((uint32_t)Tc + st - 1u) / st) : 1;
     };
     auto clamp_hist = [&](int64_t Tr) -> int64_t { return Tr < 0 ? 0 : (Tr > a.max_hist ? a.max_hist : Tr); };
-    if (a.len_first) {
+    if (mode == 1) {
         int T_early = T_in;
         asm volatile("" : "+v"(T_early));
         if (split >= splits_used(clamp_hist(T_early))) {
@@ -333,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);  // nothing below moves above the check
     const int64_t tile0 = t0 / kTileTokens;
-    const int rounds = a.rounds;
+    const int rounds = mode == 2 ? RW : a.rounds;  // a device plan's splits end at t1, within RW rounds
 
     // ---- 1. loads in the order they are needed (a wave's loads retire in issue
     //         order): this thread's query values, the codebook values of this
@@ -394,12 +489,12 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     int T_v = T_in, R_v = R_in;
     asm volatile("" : "+v"(T_v), "+v"(R_v));  // first use of the lengths: here, not earlier
     const int64_t T = clamp_hist(T_v);
-    const int ns = splits_used(T);
+    const int ns = mode == 2 ? ns_dev : splits_used(T);
     if (split >= ns) {  // loads are in flight: let them land before the work-group ends
         __builtin_amdgcn_s_waitcnt(0);
         return;
     }
-    const int64_t t1 = T < t0 + a.split_tokens ? T : t0 + a.split_tokens;
+    const int64_t t1 = T < t0 + tspan ? T : t0 + tspan;
     int R = R_v;
     R = R < 0 ? 0 : (R > a.r_cap ? (int)a.r_cap : R);
     const int rs_per = (R + ns - 1) / ns;
@@ -722,8 +817,9 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     __syncthreads();
 
     // ---- 6. output partial: histogram x value codebook + recent weights x values
-    float* part = a.partials + ((int64_t)(b * a.Hq + hq0) * a.n_split + split) * a.pstride;
-    const int64_t head_step = (int64_t)a.n_split * a.pstride;
+    // partial records: one per (item, query head of the group), item = item_first + split
+    float* part = a.partials + ((int64_t)(item_first + split) * QH) * a.pstride;
+    const int64_t head_step = a.pstride;
     {
         float acc[QH][CPL];
 #pragma unroll
@@ -866,7 +962,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     if (!last_flag) return;
     // Every output element reads (max, sum, value) of eight splits at a time --
     // all loads in flight together -- and folds them in with a running max.
-    const float* prow0 = a.partials + (int64_t)(b * a.Hq + hq0) * a.n_split * a.pstride;
+    const float* prow0 = a.partials + (int64_t)item_first * QH * a.pstride;
     for (int e = tid; e < QH * D; e += kThreads) {
         const int j = e / D;
         const int el = e - j * D;
@@ -877,7 +973,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int sp = s0 + u < ns ? s0 + u : ns - 1;
-                const float* ps = prow + (int64_t)sp * a.pstride;
+                const float* ps = prow + (int64_t)sp * QH * a.pstride;
                 pm[u] = collect(ps + D);
                 pl[u] = collect(ps + D + 1);
                 po[u] = collect(ps + el);
@@ -941,7 +1037,7 @@ hipError_t launch_typed(const pqkv_dims& d, int32_t batch, const DecodePlan& pla
     k.Hkv = d.n_kv_heads;
     k.n_groups = plan.n_groups;
     k.n_split = plan.n_split;
-    k.len_first = batch > 1;
+    k.len_first = batch == 1 ? 0 : (batch <= kDevicePlanMaxBatch && in.max_hist > 0 ? 2 : 1);
     k.rounds = plan.rounds;
     k.pstride = plan.partial_stride;
     k.split_tokens = plan.split_tokens;

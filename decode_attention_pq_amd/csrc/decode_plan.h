@@ -32,6 +32,17 @@ constexpr int decode_kernel_rounds(int n_sub, int qh, int rounds) {
 // Splits per unit the merge can take (its split maxima and sums live in LDS).
 constexpr int kMaxSplits = 512;
 
+// The split plan's cost model, in units of about a twentieth of a round of streaming:
+// a work-group's fixed costs (codebooks, LUT, epilogue, merge), one round of its split,
+// one unused step of its kernel build.  The host plan and the device-side plan of
+// ragged batches price candidates with the same constants.
+constexpr int kPlanFixed = 48;
+constexpr int kPlanRound = 20;
+constexpr int kPlanUnused = 3;
+// Batches of 2 to this many sequences plan their splits on the device, from the
+// actual lengths: every work-group reads them all and prices each round count.
+constexpr int kDevicePlanMaxBatch = 16;
+
 // How a decode call is cut into work-groups.
 struct DecodePlan {
     int qh;              // query heads per work-group (share one kv head)
