@@ -65,7 +65,9 @@ __global__ __launch_bounds__(kAppThreads) void roll_kernel(AppendArgs a) {
     constexpr int MW = SW / kAppWaves;       // subspaces per wave
     constexpr int CS = SW * DSUB;            // floats per staged centroid row
     static_assert(M % SW == 0 && SW % kAppWaves == 0, "roll subspace split");
-    constexpr int PAD = 4;                   // floats after every 16 centroid rows (bank spread)
+    // floats after every 16 centroid rows: sub-block b of the rescan starts on bank
+    // PAD*b mod 32, which tiles the 32 banks with the 8-byte reads of d_sub 2 at 2
+    constexpr int PAD = DSUB == 2 ? 2 : 4;
     __shared__ __align__(16) float cbs[kLdsRows * CS + kLdsRows / 16 * PAD];
     const int g = blockIdx.x % (M / SW);     // subspace group
     const int rb = blockIdx.x / (M / SW);    // block of 64 rolled rows

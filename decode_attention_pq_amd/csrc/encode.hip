@@ -27,9 +27,13 @@ constexpr int kEncThreads = 1024;
 // as the registers of four waves per SIMD hold
 template <int DSUB>
 constexpr int enc_tokens_per_lane() { return DSUB == 2 ? 4 : 2; }
-// floats between sub-blocks of 16 centroid rows in LDS: the sub-blocks that the
-// lanes of a wave rescan start on different banks
-constexpr int kEncPad = 4;
+// floats between sub-blocks of 16 centroid rows in LDS, so that the sub-blocks the
+// lanes of a half-wave rescan sit on different banks: the codebook rows are a
+// multiple of 32 banks long, so sub-block b starts on bank PAD*b mod 32 -- with 2
+// floats (d_sub 2, 8-byte reads) the 16 sub-blocks of 256 centroids tile the 32
+// banks; 16-byte reads (d_sub 4) need 4
+template <int DSUB>
+constexpr int enc_pad() { return DSUB == 2 ? 2 : 4; }
 
 template <int D, int DSUB, typename XT>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(
@@ -37,14 +41,15 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const float* __restrict__ cb, int K, int Hkv, uint8_t* __restrict__ codes, int64_t t_cap,
     int64_t t_start) {
     constexpr int M = D / DSUB;
-    // [c][m][j], the global layout, with kEncPad floats after every 16 centroid rows
-    __shared__ float4 cbs4[(kLdsRows * D + kLdsRows / 16 * kEncPad) / 4];
-    const float* cbs = reinterpret_cast<const float*>(cbs4);
+    constexpr int PAD = enc_pad<DSUB>();
+    // [c][m][j], the global layout, with PAD floats after every 16 centroid rows
+    __shared__ float2 cbs2[(kLdsRows * D + kLdsRows / 16 * PAD) / 2];
+    const float* cbs = reinterpret_cast<const float*>(cbs2);
 
     const int h = blockIdx.y;
     const int b = blockIdx.z;
-    const float4* src = reinterpret_cast<const float4*>(cb + (int64_t)h * K * D);
-    for (int i = threadIdx.x; i < K * D / 4; i += kEncThreads) cbs4[i + i / (4 * D) * (kEncPad / 4)] = src[i];
+    const float2* src = reinterpret_cast<const float2*>(cb + (int64_t)h * K * D);
+    for (int i = threadIdx.x; i < K * D / 2; i += kEncThreads) cbs2[i + i / (8 * D) * (PAD / 2)] = src[i];
     __syncthreads();
 
     // tokens i, i + kEncThreads, ... of the work-group's block
@@ -80,7 +85,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
             load_sub<DSUB>(row[n] + (m + 1 < M ? m + 1 : m) * DSUB, nxt[n]);
         }
         int code[NT];
-        nearest_codes<DSUB, D, kEncPad, NT>(xs, cbs + m * DSUB, K, code);
+        nearest_codes<DSUB, D, PAD, NT>(xs, cbs + m * DSUB, K, code);
 #pragma unroll
         for (int n = 0; n < NT; ++n)
             if (live[n]) put_code<M>(dst[n], slot[n], m, code[n]);
