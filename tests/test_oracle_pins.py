@@ -560,6 +560,37 @@ def test_generator_chunks_draw_alone():
     assert len(synthkv.sample_chunks(11, 1000)) == 1
 
 
+def test_numpy_mini_oracle_rederives_tiny(oracle_mod):
+    """The Tiny workload computed twice, by the C oracle and by the NumPy mini-oracle
+    (oracle/mini.py, written apart from it): the same fp32 codebooks bit for bit (same
+    operations in the same order), the same codes and best distances, and the same
+    attention within 1e-12."""
+    from oracle import mini
+
+    w = synthkv.WORKLOADS["tiny"]
+    cbs, codes = {}, {}
+    for tensor in ("k", "v"):
+        values = synthkv.calibration_kv(w, 0, tensor)
+        order = synthkv.init_order(w, 0, tensor, values.shape[0])
+        cb_c = oracle.fit_codebooks(values, w.d_sub, w.n_centroids, w.kmeans_iters, order)
+        cb_n = mini.fit_codebooks(values, w.d_sub, w.n_centroids, w.kmeans_iters, order)
+        np.testing.assert_array_equal(cb_c.view(np.uint32), cb_n.view(np.uint32))
+        x = synthkv.history_kv(w, 0, tensor, 0)
+        c_c, d1, _, _ = oracle.encode(x, cb_c)
+        c_n, d_n = mini.encode(x, cb_n)
+        np.testing.assert_array_equal(c_c, c_n)
+        np.testing.assert_array_equal(d1, d_n)
+        cbs[tensor], codes[tensor] = cb_c, c_c.transpose(1, 0, 2)  # [H, T, M]
+    q = synthkv.queries(w)
+    rk, rv = synthkv.recent_kv(w, 0, "k"), synthkv.recent_kv(w, 0, "v")
+    scale = float(np.float32(1.0 / np.sqrt(w.head_dim)))
+    ref_out, ref_lse = oracle.decode_exact(q, cbs["k"], cbs["v"], codes["k"][None], codes["v"][None], w.hist_len,
+                                           rk, rv, [w.recent_len], scale)
+    out, lse = mini.decode(q[0], cbs["k"], cbs["v"], codes["k"], codes["v"], rk[0], rv[0], scale)
+    np.testing.assert_allclose(out, ref_out[0], rtol=0, atol=1e-12 * np.abs(ref_out).max())
+    np.testing.assert_allclose(lse, ref_lse[0], rtol=1e-12, atol=0)
+
+
 # ------------------------------------------------------------------ O7 live-cache step
 @pytest.mark.parametrize("r_cap,n_roll", [(5, 3), (4, 4), (3, 1)])
 def test_append_step_equals_bulk_quantisation(oracle_mod, r_cap, n_roll):
