@@ -242,6 +242,17 @@ __device__ inline void load4(const __half* p, float (&v)[4]) {
     v[3] = b.y;
 }
 
+// Issue priority of this wave on its SIMD (0-3).  The two waves of a SIMD would
+// otherwise be served oldest first, so the younger one falls behind in each phase and
+// the work-group then waits for it at the next barrier; a wave that is ahead by a
+// quarter of the phase's tiles drops a level below the other.
+__device__ inline void set_prio(int p) {
+    if (p <= 0) __builtin_amdgcn_s_setprio(0);
+    else if (p == 1) __builtin_amdgcn_s_setprio(1);
+    else if (p == 2) __builtin_amdgcn_s_setprio(2);
+    else __builtin_amdgcn_s_setprio(3);
+}
+
 struct DecArgs {
     // first 64 bytes: everything the work mapping and the first loads need, so one
     // scalar load brings it in
@@ -608,6 +619,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     float sc[RW][QH];
 #pragma unroll
     for (int s = 0; s < RW; ++s) {
+        set_prio(3 - (4 * s) / RW);
         issue(ring[(s + P) % NSLOT], s + P);
 #pragma unroll
         for (int j = 0; j < QH; ++j) sc[s][j] = -INFINITY;
@@ -656,6 +668,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         }
     }
 
+    set_prio(0);
     // ---- 4. work-group max over history and recent scores, and a bound on the
     //         history's weight sum, which sets the histogram's fixed-point scale: a
     //         lane's RW weights sum to at most RW times its largest.  Each wave takes
@@ -761,6 +774,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     for (int j = 0; j < QH; ++j) lsum[j] = 0u;
 #pragma unroll
     for (int s = RW; s < 2 * RW; ++s) {
+        set_prio(3 - (4 * (s - RW)) / RW);
         if (s + P < 2 * RW) issue(ring[(s + P) % NSLOT], s + P);  // nothing is left to request at the end
         if (step_ok(s) && step_tile(s) * kTileTokens + lane < t1) {
             const u32x4(&cw)[NCH] = ring[s % NSLOT];
@@ -798,6 +812,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
             }
         }
     }
+    set_prio(0);
     // recent weights, scaled by 2^S like the histogram
 #pragma unroll
     for (int j = 0; j < QH; ++j) {
