@@ -324,8 +324,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     // Items run head-major (all sequences of kv head 0, then of head 1, ...), so
     // every XCD gets a share of every sequence even when their lengths differ.
     const int L = blockIdx.x;
-    const int xcd = L & 7;
-    int item = xcd * (a.n_items >> 3) + (xcd < (a.n_items & 7) ? xcd : (a.n_items & 7)) + (L >> 3);
+    int item = xcd_item(L, a.n_items);
     const int batch = a.n_items / (a.Hkv * a.n_groups * a.n_split);
     // This work-group's piece: sequence b, kv head h, query-head group grp, split
     // `split` of the sequence's ns_dev splits (device plan) starting at token t0 and at
@@ -371,9 +370,8 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         // XCD x takes ceil((used - x) / 8) of them; the grid's other work-groups exit
         // (nothing issued yet but the lengths, which have landed)
         const int used = a.Hkv * a.n_groups * (int)Sb;
-        const int slot = L >> 3;
-        if (slot >= (used - xcd + 7) / 8) return;
-        item = xcd * (used >> 3) + (xcd < (used & 7) ? xcd : (used & 7)) + slot;
+        if (!xcd_has_item(L, used)) return;
+        item = xcd_item(L, used);
         const int hg = item / (int)Sb;
         const int kk = item - hg * (int)Sb;
         int acc = 0, bq = 0;

@@ -29,6 +29,18 @@ constexpr int decode_kernel_rounds(int n_sub, int qh, int rounds) {
     return n_sub == 64 ? (rounds <= 2 ? 2 : rounds <= 4 ? 4 : rounds <= 8 ? 8 : rounds <= 12 ? 12 : 16)
                        : (rounds <= 4 ? 4 : decode_max_rounds(n_sub, qh));
 }
+// Work-group id -> work item of a grid of n items: ids that share an XCD (id mod 8,
+// the order in which the hardware deals work-groups out to the 8 XCDs) take contiguous
+// items, XCD x holding ceil((n - x) / 8) of them, so the splits of one kv head meet in
+// one L2.  Ids below n map one to one onto [0, n).
+constexpr int xcd_item(int id, int n) {
+    const int x = id & 7;
+    return x * (n >> 3) + (x < (n & 7) ? x : (n & 7)) + (id >> 3);
+}
+// Whether work-group `id` has an item when only the first `used` of the grid's items
+// exist (the device-side plan may need fewer than the host launched).
+constexpr bool xcd_has_item(int id, int used) { return (id >> 3) < (used - (id & 7) + 7) / 8; }
+
 // Splits per unit the merge can take (its split maxima and sums live in LDS).
 constexpr int kMaxSplits = 512;
 

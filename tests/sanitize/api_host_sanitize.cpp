@@ -102,6 +102,34 @@ int main() {
                                                                                f.partial_stride * 4);
                         }
 
+    // work-group id -> item: every grid size maps its ids one to one onto its items, XCD
+    // x (id mod 8) holding a contiguous block of ceil((n - x) / 8); with only `used` of
+    // the items live (the device-side plan), exactly the ids that xcd_has_item keeps
+    // cover [0, used) once each, in the same contiguous blocks
+    for (int n = 1; n <= 4100; ++n) {
+        std::vector<int> seen(n, 0);
+        bool ok = true;
+        for (int id = 0; id < n; ++id) {
+            const int it = xcd_item(id, n);
+            ok = ok && it >= 0 && it < n && !seen[it]++;
+            const int x = id & 7, lo = x * (n >> 3) + (x < (n & 7) ? x : (n & 7));
+            ok = ok && it - lo == (id >> 3) && (id >> 3) < (n - x + 7) / 8;
+        }
+        CHECK(ok);
+        for (int used : {1, n / 3, n - 1, n}) {
+            if (used < 1) continue;
+            std::vector<int> hit(used, 0);
+            bool ok2 = true;
+            for (int id = 0; id < n; ++id)
+                if (xcd_has_item(id, used)) {
+                    const int it = xcd_item(id, used);
+                    ok2 = ok2 && it >= 0 && it < used && !hit[it]++;
+                }
+            for (int i = 0; i < used; ++i) ok2 = ok2 && hit[i] == 1;
+            CHECK(ok2);
+        }
+    }
+
     pqkv_dims dm = {128, 2, 256, 32, 32};
     const size_t need = pqkv_decode_workspace_bytes(&dm, 1, 32768);
     CHECK(need == 256 + 32 * 8 * 132 * 4);
