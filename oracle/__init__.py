@@ -8,8 +8,8 @@ seeded input generator ``synthkv``.
 
 Precision: float64 throughout, from exact widenings of the fp16/fp32 inputs.
 
-What it computes, and where the page (page 2 of the source, the MILLION
-write-up) states it:
+What it computes, and where the page (the MILLION write-up, DAC 2025)
+states it:
 
 * O1  ``kmeans`` / ``fit_codebooks`` -- Lloyd k-means per subspace (Fig. 5
   paragraph: clustering fused channels; the paragraph after it: PQ splits the

@@ -74,9 +74,9 @@ static void nearest(const double *x, const double *C, int K, int dsub,
 }
 
 /* ------------------------------------------------------------------------ */
-/* O1: Lloyd k-means in one subspace (offline calibration; page 2, the       */
-/* paragraphs on Fig. 5 (fused-channel clustering) and Fig. 6 (offline       */
-/* codebook training)).                                                      */
+/* O1: Lloyd k-means in one subspace (offline calibration; the MILLION      */
+/* write-up, the paragraphs on Fig. 5 (fused-channel clustering) and Fig. 6  */
+/* (offline codebook training)).                                             */
 /* Lloyd iterations from the given centroids C (K x dsub, updated in place): */
 /* assign every point to its nearest centroid (lowest index on exact ties),  */
 /* then move every non-empty centroid to the mean of its members; an empty   */
@@ -189,8 +189,8 @@ int orc_fit_codebooks(const float *X, int64_t N, int H, int d, int dsub, int K, 
 }
 
 /* ------------------------------------------------------------------------ */
-/* O2: brute-force encode (online prefill quantisation: page 2, Fig. 6       */
-/* paragraph).  For every (token, head, subspace) the code is the lowest     */
+/* O2: brute-force encode (online prefill quantisation: the MILLION         */
+/* write-up, Fig. 6 paragraph).  For every (token, head, subspace) the code is the lowest     */
 /* index attaining the minimum squared distance, evaluated over all K.       */
 /*   x      fp32 [N][H][d]                                                   */
 /*   cb     fp32 [H][K][M][dsub]                                             */
@@ -247,8 +247,8 @@ int orc_code_distance(const float *x, int64_t N, int H, int d, int dsub, int K, 
 
 /* ------------------------------------------------------------------------ */
 /* O3 + O4: dequantise, then exact softmax attention (the plain definition   */
-/* of what the blockwise history / recent-token attention of page 2, Fig. 7 */
-/* paragraph, computes as a whole).  The decode query attends to every       */
+/* of what the blockwise history / recent-token attention of the MILLION    */
+/* write-up, Fig. 7 paragraph, computes as a whole).  The decode query attends to every       */
 /* cached token: the T_b history tokens (dequantised from their codes) and   */
 /* the R_b recent full-precision tokens.                                     */
 /*   q        fp32 [B][Hq][d]                                                */

@@ -1,7 +1,7 @@
 """Pins of the CPU oracle to things other than itself.
 
-Each test ties an oracle function to what the MILLION page (page 2 of the
-source: the DAC 2025 write-up) or plain mathematics fixes: closed forms, the
+Each test ties an oracle function to what the MILLION page (the DAC 2025
+write-up) or plain mathematics fixes: closed forms, the
 page's stated figures, textbook special cases, library routines (scipy,
 scikit-learn, torch) and brute force on tiny inputs.  A plausible mistake in
 the oracle (a dropped term, a wrong sign or index, a transposed operand) should
