@@ -175,6 +175,14 @@ DECODE_CASES = [
     (128, 2, 96, 32, 32, (4500, 4400, 4097, 1, 0, 4500, 3000, 4499), (1, 0) * 4, 4, np.float16),
     # d_sub 4, two query heads per work-group, 10 rounds in the 16-round build
     (128, 4, 256, 32, 8, (20000, 19000, 300, 20000), (5, 0, 9, 2), 16, np.float16),
+    # the device-side split plan at its largest batch (16 ragged sequences, empty ones and
+    # tile edges among them), one sequence more (the host plan again), and 16 equal
+    # lengths (the device plan keeps the host's)
+    (128, 2, 256, 4, 4, (9000, 0, 1, 64, 65, 4096, 4097, 300, 8191, 8192, 2, 1000, 7000, 513, 0, 3333),
+     (1, 2, 0, 8, 3, 0, 5, 8, 1, 0, 2, 7, 0, 4, 6, 8), 8, np.float16),
+    (128, 2, 256, 4, 4, (9000, 0, 1, 64, 65, 4096, 4097, 300, 8191, 8192, 2, 1000, 7000, 513, 0, 3333, 5000),
+     (1, 2, 0, 8, 3, 0, 5, 8, 1, 0, 2, 7, 0, 4, 6, 8, 3), 8, np.float16),
+    (128, 4, 256, 8, 2, (3000,) * 16, (2,) * 16, 4, np.float16),
 ]
 
 
