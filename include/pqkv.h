@@ -178,8 +178,11 @@ size_t pqkv_decode_workspace_bytes(const pqkv_dims* dims, int32_t batch, int64_t
  * lengths (max_hist_len, fixed at capture, must still bound them).
  * Device-side lengths outside their bounds are clamped to them.  Errors: INVALID
  * for null pointers, misaligned pointers, negative sizes, max_hist_len > t_cap, bad
- * dtype; UNSUPPORTED for dims outside the ranges above, r_cap > PQKV_MAX_RECENT, or a
- * lut with K % 4 != 0; WORKSPACE for a missing, short or misaligned workspace.
+ * dtype; UNSUPPORTED for dims outside the ranges above, r_cap > PQKV_MAX_RECENT, a
+ * lut with K % 4 != 0, or a max_hist_len that needs more than 512 splits per (sequence,
+ * kv head, query-head group): above 4,194,304 tokens, or 2,097,152 where four query
+ * heads share a work-group (n_q_heads / n_kv_heads a multiple of 4 with head_dim / d_sub
+ * <= 16); WORKSPACE for a missing, short or misaligned workspace.
  */
 pqkv_status pqkv_decode_attention(const pqkv_dims* dims, int32_t batch, const void* q,
                                   pqkv_dtype q_dtype, const float* lut, const float* codebook_k,

@@ -136,6 +136,15 @@ def test_split_plan_choices(P):
     assert need == pad(611 * 528) + 256
     assert L.pqkv_decode_attention(_d(P, 128, 2, 256, 1, 1), 1, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, 5000000, FAKE,
                                    5000000, FAKE, FAKE, 0, 0, FAKE, 0.088, FAKE, FAKE, FAKE, need, None) == 2
+    # the limit itself: 512 splits of 16 rounds (8192 tokens) with one or two query heads
+    # per work-group, of 8 rounds with four; one token more is refused
+    for dims, limit in (((128, 2, 256, 1, 1), 512 * 8192), ((64, 4, 256, 4, 1), 512 * 4096)):
+        assert ws(dims, 1, limit) == pad(512 * (dims[0] + 4) * 4 * dims[3]) + 256
+        for maxh, status in ((limit + 1, 2), (limit + 64, 2)):
+            w_need = ws(dims, 1, maxh)
+            assert L.pqkv_decode_attention(_d(P, *dims), 1, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, limit + 64, FAKE,
+                                           maxh, FAKE, FAKE, 0, 0, FAKE, 0.088, FAKE, FAKE, FAKE, w_need,
+                                           None) == status
 
 
 def test_noalloc_refuses_sizes_beyond_its_array(P):
