@@ -1,0 +1,326 @@
+// pq_encode on the matrix cores, for subspaces of dimension 4 and 256 centroids.
+//
+// MILLION write-up (DAC 2025), page "MILLION": the paragraph after Fig. 5 splits the
+// head vector into subspaces of dimension 2 or 4; the Fig. 6 paragraph encodes the
+// prefill KV cache with the offline-trained codebooks.  The code of a subvector is
+// the index of the centroid at the smallest squared Euclidean distance, the lowest
+// index winning exact ties.  The codes are those of the direct scan (nearest_codes):
+// the decision is always taken on the fp32 distances sum_j (x_j - c_j)^2, and the
+// matrix cores only narrow down where to look.
+//
+// Why the matrix cores: up to the common |x|^2, the distances of a subvector x to the
+// centroids c are |c|^2 - 2 c.x, and for 16 centroids and 16 tokens the c.x part is a
+// 16x16x4 product (one v_mfma_f32_16x16x4f32, K = 4 = d_sub) whose accumulator input
+// adds |c|^2.  At d_sub 4 the direct scan spends about 9 VALU lane-operations per
+// (subvector, centroid) pair; here the products replace most of them.  (At d_sub 2 the
+// direct scan needs about 5, which the products and their share of bookkeeping do not
+// beat: the products and the vector work issue one after the other on a SIMD.)
+//
+// Pass 1 (matrix cores).  Lane l of a wave holds token j = l % 16 of a group of 16
+// tokens and, of every block of 16 centroids, the 4 centroids 4g..4g+3 with
+// g = l / 16 (the layout of the product's result).  For each block it takes the
+// minimum over its 4 of
+//     L_c = (1 - 2^-19) |c|^2 - 2 c.x + X'      (rounded fp32, as the product gives it)
+// and keeps the smallest of those minima (its best group) and the second smallest.
+// X' = X + 2^-17 (X + max |c|^2) with X = |x|^2 is the same for all centroids of a
+// token; it makes every L positive (its exact value is at least 2^-17 X + 3 * 2^-19
+// |c|^2, above the rounding), so the minima are taken on the bit patterns as integers,
+// which order positive floats as floats do, with no NaN handling per value.  NaN or
+// infinite inputs make X' or the bound below non-finite and take the direct scan.
+//
+// Pass 2 (exact).  Every lane computes the direct fp32 distances of its best group's
+// 4 centroids; the 4 lanes of a token then keep the smallest distance, the lowest
+// index on ties.  That is the direct scan's code whenever every centroid that could
+// win lies in one of those groups, which the following bound establishes.
+//
+// The bound.  With u = 2^-24: |c|^2 is rounded 4 times, then scaled and added to X'
+// (2 more), and the product sums 5 terms, so L_c is within 18u|c|^2 + 9u X of its
+// exact value; the direct distance d_c (6 rounding steps on non-negative terms) is
+// within 6u |x - c|^2 <= 12u (X + |c|^2) of |x - c|^2.  Hence
+//     L_c - 21u X  <=  d_c - X + X'  <=  L_c + 62u |c|^2 + 21u X,
+// the (1 - 2^-19) scale putting the 32u|c|^2 of slack on one side.  The direct scan's
+// winner c* has d_c* <= d_c for the centroid c of every lane's best value, so
+//     L_c* <= best_l + 62u cnmax_l + 42u X   for every lane l of the token,
+// cnmax_l the largest |c|^2 of lane l's best group.  Candidates are therefore the
+// groups whose value is at most
+//     thr = min over the token's lanes of (best_l + 2^-17 cnmax_l) + 2^-17 X
+// (2^-17 = 128u: twice the 62u and three times the 42u).  A lane whose second smallest
+// group value is also <= thr -- a near tie, a fraction of a percent of the subvectors
+// -- or a bound that is not finite sends the wave's groups to the direct scan of all
+// 256 centroids, which gives the direct scan's codes by construction.
+//
+// Work decomposition (gfx950): one work-group of 512 threads (8 waves) per (2048
+// tokens, kv head, half of the subspaces, sequence).  The half's codebook is staged
+// once in LDS as the product's operand rows: per (subspace, block of 16 centroids),
+// component k of centroid i at word 16k + i, then the scaled |c|^2 of centroid i.  A
+// wave takes two groups of 16 tokens at a time -- they share the operand reads and
+// give it two independent chains -- and walks the subspaces for them.
+
+#include "nearest.h"
+
+namespace pqkv {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMfDsub = 4;
+constexpr int kMfThreads = 512;
+constexpr int kMfWaves = kMfThreads / 64;
+constexpr int kMfGroups = 16;                          // groups of 16 tokens per wave
+constexpr int kMfTokens = kMfWaves * kMfGroups * 16;   // tokens per work-group
+constexpr int kMfBlocks = 16;                          // blocks of 16 centroids (K = 256)
+constexpr int kMfWords = 16 * (kMfDsub + 1);           // operand-row words per (subspace, block)
+constexpr int kMfCn = 16 * kMfDsub;                    // word of |c|^2 in a row
+constexpr int kMfSlices = 2;                           // subspace halves per kv head
+
+// the (1 - 2^-19) scale of |c|^2 in the operand rows, and the bound's 2^-17
+constexpr float kCnScale = 1.0f - 0x1p-19f;
+constexpr float kBound = 0x1p-17f;
+
+// Minimum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the 4 lanes of a token).  A
+// permlane swap of a value with itself leaves each lane its own value and its
+// partner's, in an order that depends on the row; the minimum of the two does not.
+__device__ inline float lanes_min(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fminf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// The same for (distance, index) pairs: the smaller distance, the lower index on
+// equal ones (an order that does not depend on which of the two is the lane's own).
+__device__ inline void lanes_argmin(float& d, int& i) {
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+        const auto pd = step == 0 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(d), __float_as_uint(d), false, false)
+                                  : __builtin_amdgcn_permlane32_swap(__float_as_uint(d), __float_as_uint(d), false, false);
+        const auto pi = step == 0 ? __builtin_amdgcn_permlane16_swap((uint32_t)i, (uint32_t)i, false, false)
+                                  : __builtin_amdgcn_permlane32_swap((uint32_t)i, (uint32_t)i, false, false);
+        const float d0 = __uint_as_float(pd[0]), d1 = __uint_as_float(pd[1]);
+        const int i0 = (int)pi[0], i1 = (int)pi[1];
+        const bool other = d1 < d0 || (d1 == d0 && i1 < i0);
+        d = other ? d1 : d0;
+        i = other ? i1 : i0;
+    }
+}
+
+// Direct distances of one token's subvector to centroids c0 .. c0 + 3 (c0 a multiple of
+// 4) of the staged rows `rows` of one subspace, strict < in ascending order: the
+// running (distance, index) pair changes only for a smaller distance, so equal ones
+// keep the lowest index and NaN distances never win.
+__device__ inline void direct_scan_group(const float (&xs)[kMfDsub], const float* rows, int c0, float& bd, int& bi) {
+    const float* r = rows + (c0 >> 4) * kMfWords + (c0 & 15);
+    float cv[4][kMfDsub];
+#pragma unroll
+    for (int k = 0; k < kMfDsub; ++k) {  // 4 consecutive centroids: one 16-byte read per component
+        const float4 v = *reinterpret_cast<const float4*>(r + 16 * k);
+        cv[0][k] = v.x;
+        cv[1][k] = v.y;
+        cv[2][k] = v.z;
+        cv[3][k] = v.w;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float dd = sq_dist<kMfDsub>(xs, cv[q]);
+        const bool take = dd < bd;
+        bd = take ? dd : bd;
+        bi = take ? c0 + q : bi;
+    }
+}
+
+template <int D, typename XT>
+__global__ __launch_bounds__(kMfThreads) void encode_mfma_kernel(
+    const XT* __restrict__ x, int64_t n_tokens, int64_t s_seq, int64_t s_tok, int64_t s_head,
+    const float* __restrict__ cb, int Hkv, uint8_t* __restrict__ codes, int64_t t_cap, int64_t t_start) {
+    constexpr int DSUB = kMfDsub;
+    constexpr int M = D / DSUB;
+    constexpr int MH = M / kMfSlices;  // subspaces of this work-group's half
+    constexpr int K = kMfBlocks * 16;
+    constexpr int W = kMfWords;
+    __shared__ __align__(16) float rows[MH * kMfBlocks * W];  // [subspace][block][W]
+    __shared__ uint32_t cnmax_bits[MH];  // per subspace: max scaled |c|^2 (bits; NaN above all)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int h = blockIdx.y / kMfSlices;
+    const int m0 = (blockIdx.y % kMfSlices) * MH;
+    const int b = blockIdx.z;
+
+    // ---- stage the half's codebook as operand rows.  Consecutive threads take
+    // consecutive centroids of one block, so the LDS stores are conflict-free.
+    for (int i = tid; i < MH; i += kMfThreads) cnmax_bits[i] = 0u;
+    __syncthreads();
+    const float* cbh = cb + (int64_t)h * K * M * DSUB;
+    for (int e = tid; e < kMfBlocks * MH * 16; e += kMfThreads) {
+        const int i = e & 15;
+        const int mm = (e >> 4) % MH;
+        const int bb = (e >> 4) / MH;
+        const int c = bb * 16 + i;
+        float v[DSUB];
+        load_sub<DSUB>(cbh + ((int64_t)c * M + m0 + mm) * DSUB, v);
+        float cn = v[0] * v[0];
+#pragma unroll
+        for (int k = 1; k < DSUB; ++k) cn = fmaf(v[k], v[k], cn);
+        float* r = rows + (mm * kMfBlocks + bb) * W;
+#pragma unroll
+        for (int k = 0; k < DSUB; ++k) r[16 * k + i] = v[k];
+        r[kMfCn + i] = cn * kCnScale;
+        atomicMax(&cnmax_bits[mm], __float_as_uint(cn * kCnScale));  // non-negative: uint order
+    }
+    __syncthreads();
+
+    const int j = lane & 15;  // token of the group
+    const int g = lane >> 4;  // lane group: centroids 4g..4g+3 of every block; product row k = g
+    uint8_t* plane = codes + ((int64_t)b * Hkv + h) * t_cap * M;
+    const XT* xh = x + (int64_t)b * s_seq + (int64_t)h * s_head + m0 * DSUB;
+
+    constexpr int NG = 2;  // groups of 16 tokens at a time
+    for (int grp = 0; grp < kMfGroups; grp += NG) {
+        const int64_t t16 = (int64_t)blockIdx.x * kMfTokens + (int64_t)(grp * kMfWaves + wave) * 16;
+        if (t16 >= n_tokens) break;  // the same for the whole wave
+        bool live[NG];
+        const XT* row[NG];
+        uint8_t* dst[NG];
+        int slot[NG];
+        float xn[NG][DSUB];
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            const int64_t tk = t16 + (int64_t)q * kMfWaves * 16 + j;
+            live[q] = tk < n_tokens;
+            const int64_t tl = live[q] ? tk : n_tokens - 1;  // a missing token repeats the last one
+            row[q] = xh + tl * s_tok;
+            dst[q] = code_slot<M>(plane, t_start + tl);
+            slot[q] = (int)((t_start + tl) & (kTileTokens - 1));
+            load_sub<DSUB>(row[q], xn[q]);
+        }
+#pragma unroll 1
+        for (int mm = 0; mm < MH; ++mm) {
+            const float* rm = rows + mm * kMfBlocks * W;
+            // every block's operand value (component g of centroid j) and the scaled
+            // |c|^2 of this lane's 4 centroids, requested first
+            float av[kMfBlocks];
+            float4 cnv[kMfBlocks];
+#pragma unroll
+            for (int bb = 0; bb < kMfBlocks; ++bb) {
+                av[bb] = rm[bb * W + lane];
+                cnv[bb] = *reinterpret_cast<const float4*>(rm + bb * W + kMfCn + 4 * g);
+            }
+            const float cnsub = __uint_as_float(cnmax_bits[mm]);
+            float xs[NG][DSUB], xx[NG], xoff[NG], bv[NG];
+#pragma unroll
+            for (int q = 0; q < NG; ++q) {
+#pragma unroll
+                for (int k = 0; k < DSUB; ++k) xs[q][k] = xn[q][k];
+                load_sub<DSUB>(row[q] + (mm + 1 < MH ? mm + 1 : mm) * DSUB, xn[q]);  // the next subvector
+                float xg = xs[q][0];  // component g of token j: the product's row k = g
+#pragma unroll
+                for (int k = 1; k < DSUB; ++k) xg = g == k ? xs[q][k] : xg;
+                bv[q] = -2.0f * xg;
+                xx[q] = xs[q][0] * xs[q][0];
+#pragma unroll
+                for (int k = 1; k < DSUB; ++k) xx[q] = fmaf(xs[q][k], xs[q][k], xx[q]);
+                xoff[q] = fmaf(kBound, xx[q] + cnsub, xx[q]);
+            }
+
+            // ---- pass 1: the lane's value of every block, its best and second best
+            int best[NG], second[NG], bidx[NG];
+#pragma unroll
+            for (int q = 0; q < NG; ++q) {
+                best[q] = 0x7fffffff;
+                second[q] = 0x7fffffff;
+                bidx[q] = 0;
+            }
+#pragma unroll
+            for (int bb = 0; bb < kMfBlocks; ++bb) {
+#pragma unroll
+                for (int q = 0; q < NG; ++q) {
+                    const f32x4 c4 = {cnv[bb].x + xoff[q], cnv[bb].y + xoff[q], cnv[bb].z + xoff[q],
+                                      cnv[bb].w + xoff[q]};
+                    const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[bb], bv[q], c4, 0, 0, 0);
+                    const int a0 = __float_as_int(acc[0]), a1 = __float_as_int(acc[1]);
+                    const int a2 = __float_as_int(acc[2]), a3 = __float_as_int(acc[3]);
+                    const int t = min(min(a0, a1), min(a2, a3));
+                    bidx[q] = t < best[q] ? bb : bidx[q];
+                    second[q] = min(second[q], max(best[q], t));
+                    best[q] = min(best[q], t);
+                }
+                // at most 4 blocks' products in flight: their results stay in registers
+                if (bb % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+            // ---- the bound, over the token's 4 lanes
+            bool wide = false;
+#pragma unroll
+            for (int q = 0; q < NG; ++q) {
+                const float4 v = *reinterpret_cast<const float4*>(rm + bidx[q] * W + kMfCn + 4 * g);
+                const float cnmax = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+                const float lim = lanes_min(fmaf(kBound, cnmax, __int_as_float(best[q])));
+                const float thr = fmaf(kBound, xx[q], lim) + 1e-30f;
+                wide = wide || !(thr < INFINITY) || !(xoff[q] < INFINITY) || __int_as_float(second[q]) <= thr;
+            }
+
+            // ---- pass 2: direct distances of the candidates
+            float bd[NG];
+            int bi[NG];
+#pragma unroll
+            for (int q = 0; q < NG; ++q) {
+                bd[q] = INFINITY;
+                bi[q] = 0x7fffffff;
+            }
+            if (__any(wide)) {
+                // every lane scans its 4 centroids of every block
+#pragma unroll 1
+                for (int bb = 0; bb < kMfBlocks; ++bb)
+#pragma unroll
+                    for (int q = 0; q < NG; ++q) direct_scan_group(xs[q], rm, bb * 16 + 4 * g, bd[q], bi[q]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < NG; ++q) direct_scan_group(xs[q], rm, bidx[q] * 16 + 4 * g, bd[q], bi[q]);
+            }
+#pragma unroll
+            for (int q = 0; q < NG; ++q) {
+                lanes_argmin(bd[q], bi[q]);
+                // no distance below +inf: code 0, as the direct scan gives
+                if (g == 0 && live[q]) put_code<M>(dst[q], slot[q], m0 + mm, bd[q] < INFINITY ? bi[q] : 0);
+            }
+        }
+    }
+}
+
+template <int D, typename XT>
+hipError_t launch_typed(const pqkv_dims& d, const void* x, int32_t n_seqs, int64_t n_tokens, int64_t s_seq,
+                        int64_t s_tok, int64_t s_head, const float* cb, uint8_t* codes, int64_t t_cap,
+                        int64_t t_start, hipStream_t stream) {
+    dim3 grid((unsigned)((n_tokens + kMfTokens - 1) / kMfTokens), (unsigned)(d.n_kv_heads * kMfSlices),
+              (unsigned)n_seqs);
+    hipLaunchKernelGGL((encode_mfma_kernel<D, XT>), grid, dim3(kMfThreads), 0, stream, static_cast<const XT*>(x),
+                       n_tokens, s_seq, s_tok, s_head, cb, d.n_kv_heads, codes, t_cap, t_start);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_head_dim(const pqkv_dims& d, const void* x, pqkv_dtype xt, int32_t n_seqs, int64_t n_tokens,
+                           int64_t s_seq, int64_t s_tok, int64_t s_head, const float* cb, uint8_t* codes,
+                           int64_t t_cap, int64_t t_start, hipStream_t stream) {
+    if (xt == PQKV_F16)
+        return launch_typed<D, __half>(d, x, n_seqs, n_tokens, s_seq, s_tok, s_head, cb, codes, t_cap, t_start,
+                                       stream);
+    return launch_typed<D, float>(d, x, n_seqs, n_tokens, s_seq, s_tok, s_head, cb, codes, t_cap, t_start, stream);
+}
+
+}  // namespace
+
+bool encode_mfma_supported(const pqkv_dims& d) {
+    return d.d_sub == kMfDsub && d.n_centroids == kMfBlocks * 16 && (d.head_dim == 128 || d.head_dim == 64);
+}
+
+hipError_t launch_encode_mfma(const pqkv_dims& d, const void* x, pqkv_dtype xt, int32_t n_seqs, int64_t n_tokens,
+                              int64_t s_seq, int64_t s_tok, int64_t s_head, const float* cb, uint8_t* codes,
+                              int64_t t_cap, int64_t t_start, hipStream_t stream) {
+    if (d.head_dim == 128)
+        return launch_head_dim<128>(d, x, xt, n_seqs, n_tokens, s_seq, s_tok, s_head, cb, codes, t_cap, t_start,
+                                    stream);
+    return launch_head_dim<64>(d, x, xt, n_seqs, n_tokens, s_seq, s_tok, s_head, cb, codes, t_cap, t_start, stream);
+}
+
+}  // namespace pqkv

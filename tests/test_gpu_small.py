@@ -89,6 +89,34 @@ def test_encode_duplicate_centroids_lowest_index(K, keep, dups):
     assert np.all(got == keep)
 
 
+@pytest.mark.parametrize("keep,dups", [(70, (130, 200, 255)), (100, (3, 250)), (17, (16, 18, 19)),
+                                       (240, (0, 241, 255)), (5, (6, 7, 21, 37))])
+@pytest.mark.parametrize("d", [128, 64])
+def test_encode_ties_at_dsub4(d, keep, dups):
+    # d_sub 4 with 256 centroids (the matrix-core encode): exact copies of one centroid
+    # in the same group of 4, in other groups of the same block, in other blocks, and
+    # below its index -- the lowest index of the copies wins -- and near copies (a few
+    # ulp away) whose codes must lie in the oracle's ambiguity band
+    dsub, K, H = 4, 256, 2
+    M = d // dsub
+    cb = _codebook(11 + keep, H, K, M, dsub)
+    for c in dups:
+        cb[:, c] = cb[:, keep]
+    x = np.repeat(cb[:, keep][None], 70, axis=0).reshape(70, H, d).astype(np.float32)
+    planes = run_gpu_encode(dims_for(d, dsub, K, H, H), x[None], cb, 1, 128)
+    got = oracle.untile_codes(planes[0], 70, M)
+    assert np.all(got == min((keep,) + tuple(dups)))
+    # near copies: each copy moved by a few ulp in one component
+    cb2 = cb.copy()
+    for n, c in enumerate(dups):
+        cb2[:, c, :, n % dsub] = np.nextafter(np.nextafter(cb[:, c, :, n % dsub], np.inf), np.inf)
+    x2 = x + np.float32(1e-3) * synthkv.small_normal(keep, x.shape)
+    planes = run_gpu_encode(dims_for(d, dsub, K, H, H), x2[None], cb2, 1, 128)
+    got = oracle.untile_codes(planes[0], 70, M).transpose(1, 0, 2)
+    ref, d1, d2, _ = oracle.encode(x2, cb2)
+    check_codes(got, x2, cb2, ref, d1, d2)
+
+
 @pytest.mark.parametrize("K", [256, 40])
 def test_encode_nan_and_inf_rows(K):
     # a NaN subvector has no nearest centroid under '<': code 0, as in the oracle; an
