@@ -33,6 +33,8 @@ FP32_VALU_PEAK_TFLOPS = 157.3
 # The same peak in VALU lane-operations (one 32-bit VALU instruction on one lane, an FMA
 # counted once): 78.65 T/s.  The encode scan is counted in these units.
 VALU_LANE_OPS_PEAK_T = FP32_VALU_PEAK_TFLOPS / 2
+# dense fp32 matrix-core peak of MI355X (published), for the d_sub 4 encode
+FP32_MFMA_PEAK_TFLOPS = 157.3
 
 
 class FenceFreeEvents:
@@ -429,6 +431,17 @@ def main():
     else:
         enc_ops_per_pair = 2 * w.d_sub + 3 + (0.3 if w.d_sub == 2 else 0.6)
     enc_tops = enc_pairs * enc_ops_per_pair / (enc_total_ms * 1e-3) / 1e12
+    enc_hbm = encode_bytes(w, enc_tokens // 2) / (enc_total_ms * 1e-3) / 1e9
+    if w.d_sub == 4 and w.n_centroids == 256:
+        # the matrix-core encode (encode_mfma_kernel): the 2 * d_sub flops of a pair are one
+        # 16x16x4 fp32 product's share; the exact rescan of the candidates is extra
+        encode = {"bound": "mfma", "kernel": "encode_mfma_kernel", "achieved": round(enc_tflops, 2),
+                  "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(enc_tflops / FP32_MFMA_PEAK_TFLOPS, 4)}
+    else:
+        encode = {"bound": "alu", "kernel": "encode_kernel", "valu_ops_per_pair": enc_ops_per_pair,
+                  "achieved": round(enc_tops, 2), "peak": round(VALU_LANE_OPS_PEAK_T, 2), "unit": "T VALU lane-ops/s",
+                  "frac": round(enc_tops / VALU_LANE_OPS_PEAK_T, 4), "flop_form_tflops": round(enc_tflops, 2),
+                  "fp32_peak_tflops": FP32_VALU_PEAK_TFLOPS}
 
     result = {
         "metric": METRIC,
@@ -456,12 +469,8 @@ def main():
                      "target_frac": 0.70, "meets_target": bool(achieved / HBM_PEAK_GBS >= 0.70)},
         "encode": {"tokens_per_s": round(enc_tok_s, 1), "ms": round(enc_total_ms, 4),
                    "what": "K+V of the history" if calls_per_step == 1 else "K+V of one layer's prefill",
-                   "tokens": enc_tokens, "bound": "alu", "valu_ops_per_pair": enc_ops_per_pair,
-                   "achieved": round(enc_tops, 2), "peak": round(VALU_LANE_OPS_PEAK_T, 2), "unit": "T VALU lane-ops/s",
-                   "frac": round(enc_tops / VALU_LANE_OPS_PEAK_T, 4),
-                   "flop_form_tflops": round(enc_tflops, 2), "fp32_peak_tflops": FP32_VALU_PEAK_TFLOPS,
-                   "hbm_gbs": round(encode_bytes(w, enc_tokens // 2) / (enc_total_ms * 1e-3) / 1e9, 1),
-                   "hbm_frac": round(encode_bytes(w, enc_tokens // 2) / (enc_total_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                   "tokens": enc_tokens, **encode, "hbm_gbs": round(enc_hbm, 1),
+                   "hbm_frac": round(enc_hbm / HBM_PEAK_GBS, 4)},
     }
     if fit is not None:
         result["fit_codebooks"] = fit
