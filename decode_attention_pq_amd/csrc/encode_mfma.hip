@@ -11,7 +11,7 @@
 // Why the matrix cores: up to the common |x|^2, the distances of a subvector x to the
 // centroids c are |c|^2 - 2 c.x, and for 16 centroids and 16 tokens the c.x part is a
 // 16x16x4 product (one v_mfma_f32_16x16x4f32, K = 4 = d_sub) whose accumulator input
-// adds |c|^2.  At d_sub 4 the direct scan spends about 9 VALU lane-operations per
+// is |c|^2.  At d_sub 4 the direct scan spends about 9 VALU lane-operations per
 // (subvector, centroid) pair; here the products replace most of them.  (At d_sub 2 the
 // direct scan needs about 5, which the products and their share of bookkeeping do not
 // beat: the products and the vector work issue one after the other on a SIMD.)
@@ -20,41 +20,47 @@
 // tokens and, of every block of 16 centroids, the 4 centroids 4g..4g+3 with
 // g = l / 16 (the layout of the product's result).  For each block it takes the
 // minimum over its 4 of
-//     L_c = (1 - 2^-19) |c|^2 - 2 c.x + X'      (rounded fp32, as the product gives it)
+//     L_c = fl(|c|^2) - 2 c.x      (rounded fp32, as the product gives it)
 // and keeps the smallest of those minima (its best group) and the second smallest.
-// X' = X + 2^-17 (X + max |c|^2) with X = |x|^2 is the same for all centroids of a
-// token; it makes every L positive (its exact value is at least 2^-17 X + 3 * 2^-19
-// |c|^2, above the rounding), so the minima are taken on the bit patterns as integers,
-// which order positive floats as floats do, with no NaN handling per value.  NaN or
-// infinite inputs make X' or the bound below non-finite and take the direct scan.
+// The minima are v_med3_f32 against -inf (a median that the compiler cannot turn back
+// into a minimum, which would need NaN-quieting moves on every operand); NaN or
+// infinite inputs make the bound below non-finite and take the direct scan.
 //
 // Pass 2 (exact).  Every lane computes the direct fp32 distances of its best group's
 // 4 centroids; the 4 lanes of a token then keep the smallest distance, the lowest
 // index on ties.  That is the direct scan's code whenever every centroid that could
 // win lies in one of those groups, which the following bound establishes.
 //
-// The bound.  With u = 2^-24: |c|^2 is rounded 4 times, then scaled and added to X'
-// (2 more), and the product sums 5 terms, so L_c is within 18u|c|^2 + 9u X of its
-// exact value; the direct distance d_c (6 rounding steps on non-negative terms) is
-// within 6u |x - c|^2 <= 12u (X + |c|^2) of |x - c|^2.  Hence
-//     L_c - 21u X  <=  d_c - X + X'  <=  L_c + 62u |c|^2 + 21u X,
-// the (1 - 2^-19) scale putting the 32u|c|^2 of slack on one side.  The direct scan's
-// winner c* has d_c* <= d_c for the centroid c of every lane's best value, so
-//     L_c* <= best_l + 62u cnmax_l + 42u X   for every lane l of the token,
-// cnmax_l the largest |c|^2 of lane l's best group.  Candidates are therefore the
-// groups whose value is at most
-//     thr = min over the token's lanes of (best_l + 2^-17 cnmax_l) + 2^-17 X
-// (2^-17 = 128u: twice the 62u and three times the 42u).  A lane whose second smallest
-// group value is also <= thr -- a near tie, a fraction of a percent of the subvectors
-// -- or a bound that is not finite sends the wave's groups to the direct scan of all
-// 256 centroids, which gives the direct scan's codes by construction.
+// The bound.  With u = 2^-24 and X = |x|^2: fl(|c|^2) (4 roundings) is within
+// 4u|c|^2 of |c|^2; the product adds four terms to it, and each of its roundings (at
+// most 8, however it orders them) is within u of a partial sum no larger than
+// |c|^2 + 2|c||x| <= 2|c|^2 + X.  So L_c is within 20u|c|^2 + 8uX of
+// E_c = |c|^2 - 2 c.x.  The direct distance d_c (6 roundings of non-negative terms)
+// is within 6u |x - c|^2 <= 12u (X + |c|^2) of |x - c|^2 = X + E_c.  Let c be the
+// centroid behind a lane's best value best_l, and c* the direct scan's winner
+// (d_c* <= d_c).  Chaining the three estimates,
+//     L_c* <= best_l + 32u |c|^2 + 32u |c*|^2 + 40u X.
+// Both norms are bounded by the token itself: |c|^2 <= 2X + 2|x - c|^2, and
+// |x - c|^2 = X + E_c is at most X + best_l to first order in u, so
+// |c|^2 <= 4X + 2 best_l; c* is no farther from x than c, so the same holds for it.
+// Hence (the u^2 terms are far inside the slack)
+//     L_c* <= best_l + 296u X + 128u best_l <= best_l + 2^-15 (X + max(best_l, 0)),
+// with 2^-15 = 512u leaving room for the rounding of the bound itself.  No
+// centroid's norm enters it, so a codebook with far-out centroids (outlier channels)
+// does not widen it.  Candidates are the groups whose value is at most
+//     thr = min over the token's lanes of (best_l + 2^-15 (X + max(best_l, 0))) + 1e-30
+// (the 1e-30 covers denormal operands, which the product may flush).  A lane whose
+// second smallest group value is also <= thr -- a near tie, a small fraction of the
+// subvectors -- a bound that is not finite (NaN or infinite inputs, overflow), or a
+// subspace with a non-finite centroid sends the wave's groups to the direct scan of
+// all 256 centroids, which gives the direct scan's codes by construction.
 //
-// Work decomposition (gfx950): one work-group of 512 threads (8 waves) per (2048
-// tokens, kv head, half of the subspaces, sequence).  The half's codebook is staged
-// once in LDS as the product's operand rows: per (subspace, block of 16 centroids),
-// component k of centroid i at word 16k + i, then the scaled |c|^2 of centroid i.  A
-// wave takes two groups of 16 tokens at a time -- they share the operand reads and
-// give it two independent chains -- and walks the subspaces for them.
+// Work decomposition (gfx950): one work-group of 1024 threads (16 waves, 4 per SIMD)
+// per (4096 tokens, kv head, half of the subspaces, sequence).  The half's codebook
+// is staged once in LDS as the product's operand rows: per (subspace, block of 16
+// centroids), component k of centroid i at word 16k + i, then fl(|c|^2) of
+// centroid i.  A wave takes one group of 16 tokens at a time and walks the subspaces
+// for it, holding one subspace's operands (80 values a lane) at a time.
 
 #include "nearest.h"
 
@@ -64,18 +70,19 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfDsub = 4;
-constexpr int kMfThreads = 512;
+constexpr int kMfThreads = 1024;
 constexpr int kMfWaves = kMfThreads / 64;
 constexpr int kMfGroups = 16;                          // groups of 16 tokens per wave
 constexpr int kMfTokens = kMfWaves * kMfGroups * 16;   // tokens per work-group
 constexpr int kMfBlocks = 16;                          // blocks of 16 centroids (K = 256)
 constexpr int kMfWords = 16 * (kMfDsub + 1);           // operand-row words per (subspace, block)
 constexpr int kMfCn = 16 * kMfDsub;                    // word of |c|^2 in a row
-constexpr int kMfSlices = 2;                           // subspace halves per kv head
+constexpr int kMfSlices = 4;                           // subspace quarters per kv head
 
-// the (1 - 2^-19) scale of |c|^2 in the operand rows, and the bound's 2^-17
-constexpr float kCnScale = 1.0f - 0x1p-19f;
-constexpr float kBound = 0x1p-17f;
+// the bound's relative slack, 2^-15, and its absolute one
+constexpr float kBound = 0x1p-15f;
+constexpr float kBoundAbs = 1e-30f;
+constexpr int kMfNg = 1;  // groups of 16 tokens a wave takes at a time
 
 // Minimum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the 4 lanes of a token).  A
 // permlane swap of a value with itself leaves each lane its own value and its
@@ -85,6 +92,13 @@ __device__ inline float lanes_min(float v) {
     v = fminf(__uint_as_float(p[0]), __uint_as_float(p[1]));
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline int lanes_min_int(int v) {
+    const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    v = min((int)p[0], (int)p[1]);
+    const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    return min((int)r[0], (int)r[1]);
 }
 
 // The same for (distance, index) pairs: the smaller distance, the lower index on
@@ -134,11 +148,11 @@ __global__ __launch_bounds__(kMfThreads) void encode_mfma_kernel(
     const float* __restrict__ cb, int Hkv, uint8_t* __restrict__ codes, int64_t t_cap, int64_t t_start) {
     constexpr int DSUB = kMfDsub;
     constexpr int M = D / DSUB;
-    constexpr int MH = M / kMfSlices;  // subspaces of this work-group's half
+    constexpr int MH = M / kMfSlices;  // subspaces of this work-group's quarter
     constexpr int K = kMfBlocks * 16;
     constexpr int W = kMfWords;
     __shared__ __align__(16) float rows[MH * kMfBlocks * W];  // [subspace][block][W]
-    __shared__ uint32_t cnmax_bits[MH];  // per subspace: max scaled |c|^2 (bits; NaN above all)
+    __shared__ uint32_t cnmax_bits[MH];  // per subspace: max |c|^2 (bits): below +inf iff all finite
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -165,8 +179,8 @@ __global__ __launch_bounds__(kMfThreads) void encode_mfma_kernel(
         float* r = rows + (mm * kMfBlocks + bb) * W;
 #pragma unroll
         for (int k = 0; k < DSUB; ++k) r[16 * k + i] = v[k];
-        r[kMfCn + i] = cn * kCnScale;
-        atomicMax(&cnmax_bits[mm], __float_as_uint(cn * kCnScale));  // non-negative: uint order
+        r[kMfCn + i] = cn;
+        atomicMax(&cnmax_bits[mm], __float_as_uint(cn));  // non-negative: uint order
     }
     __syncthreads();
 
@@ -175,7 +189,7 @@ __global__ __launch_bounds__(kMfThreads) void encode_mfma_kernel(
     uint8_t* plane = codes + ((int64_t)b * Hkv + h) * t_cap * M;
     const XT* xh = x + (int64_t)b * s_seq + (int64_t)h * s_head + m0 * DSUB;
 
-    constexpr int NG = 2;  // groups of 16 tokens at a time
+    constexpr int NG = kMfNg;
     for (int grp = 0; grp < kMfGroups; grp += NG) {
         const int64_t t16 = (int64_t)blockIdx.x * kMfTokens + (int64_t)(grp * kMfWaves + wave) * 16;
         if (t16 >= n_tokens) break;  // the same for the whole wave
@@ -197,17 +211,8 @@ __global__ __launch_bounds__(kMfThreads) void encode_mfma_kernel(
 #pragma unroll 1
         for (int mm = 0; mm < MH; ++mm) {
             const float* rm = rows + mm * kMfBlocks * W;
-            // every block's operand value (component g of centroid j) and the scaled
-            // |c|^2 of this lane's 4 centroids, requested first
-            float av[kMfBlocks];
-            float4 cnv[kMfBlocks];
-#pragma unroll
-            for (int bb = 0; bb < kMfBlocks; ++bb) {
-                av[bb] = rm[bb * W + lane];
-                cnv[bb] = *reinterpret_cast<const float4*>(rm + bb * W + kMfCn + 4 * g);
-            }
             const float cnsub = __uint_as_float(cnmax_bits[mm]);
-            float xs[NG][DSUB], xx[NG], xoff[NG], bv[NG];
+            float xs[NG][DSUB], xx[NG], bv[NG];
 #pragma unroll
             for (int q = 0; q < NG; ++q) {
 #pragma unroll
@@ -220,43 +225,54 @@ __global__ __launch_bounds__(kMfThreads) void encode_mfma_kernel(
                 xx[q] = xs[q][0] * xs[q][0];
 #pragma unroll
                 for (int k = 1; k < DSUB; ++k) xx[q] = fmaf(xs[q][k], xs[q][k], xx[q]);
-                xoff[q] = fmaf(kBound, xx[q] + cnsub, xx[q]);
             }
 
-            // ---- pass 1: the lane's value of every block, its best and second best
-            int best[NG], second[NG], bidx[NG];
+            // ---- pass 1: the lane's value of every block, its best and second best.
+            // med3 against -inf is the minimum; best <= second throughout, so
+            // med3(best, t, second) is the new second smallest.
+            float ninf = -INFINITY;
+            asm volatile("" : "+v"(ninf));  // opaque: keeps each med3 a med3
+            float best[NG], second[NG];
+            int bidx[NG];
 #pragma unroll
             for (int q = 0; q < NG; ++q) {
-                best[q] = 0x7fffffff;
-                second[q] = 0x7fffffff;
+                best[q] = INFINITY;
+                second[q] = INFINITY;
                 bidx[q] = 0;
             }
 #pragma unroll
             for (int bb = 0; bb < kMfBlocks; ++bb) {
+                // the block's operand value (component g of centroid j) and fl(|c|^2) of
+                // this lane's 4 centroids, the product's accumulator input
+                const float av = rm[bb * W + lane];
+                const float4 cn = *reinterpret_cast<const float4*>(rm + bb * W + kMfCn + 4 * g);
+                const f32x4 c4 = {cn.x, cn.y, cn.z, cn.w};
 #pragma unroll
                 for (int q = 0; q < NG; ++q) {
-                    const f32x4 c4 = {cnv[bb].x + xoff[q], cnv[bb].y + xoff[q], cnv[bb].z + xoff[q],
-                                      cnv[bb].w + xoff[q]};
-                    const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[bb], bv[q], c4, 0, 0, 0);
-                    const int a0 = __float_as_int(acc[0]), a1 = __float_as_int(acc[1]);
-                    const int a2 = __float_as_int(acc[2]), a3 = __float_as_int(acc[3]);
-                    const int t = min(min(a0, a1), min(a2, a3));
+                    const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[q], c4, 0, 0, 0);
+                    const float t = __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(acc[0], acc[1], ninf),
+                                                            __builtin_amdgcn_fmed3f(acc[2], acc[3], ninf), ninf);
                     bidx[q] = t < best[q] ? bb : bidx[q];
-                    second[q] = min(second[q], max(best[q], t));
-                    best[q] = min(best[q], t);
+                    second[q] = __builtin_amdgcn_fmed3f(best[q], t, second[q]);
+                    best[q] = __builtin_amdgcn_fmed3f(best[q], t, ninf);
                 }
                 // at most 4 blocks' products in flight: their results stay in registers
                 if (bb % 4 == 3) __builtin_amdgcn_sched_barrier(0);
             }
-            // ---- the bound, over the token's 4 lanes
-            bool wide = false;
+            // ---- the bound, over the token's 4 lanes.  A candidate lane is one whose
+            // best group value is within it; cbase is the first centroid of the
+            // candidate group with the lowest index (every token has at least one:
+            // the lane of its smallest value), and multi marks a second candidate.
+            bool wide = !(cnsub < INFINITY), multi = false;
+            int cbase[NG];
 #pragma unroll
             for (int q = 0; q < NG; ++q) {
-                const float4 v = *reinterpret_cast<const float4*>(rm + bidx[q] * W + kMfCn + 4 * g);
-                const float cnmax = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
-                const float lim = lanes_min(fmaf(kBound, cnmax, __int_as_float(best[q])));
-                const float thr = fmaf(kBound, xx[q], lim) + 1e-30f;
-                wide = wide || !(thr < INFINITY) || !(xoff[q] < INFINITY) || __int_as_float(second[q]) <= thr;
+                const float thr = lanes_min(fmaf(kBound, xx[q] + fmaxf(best[q], 0.0f), best[q])) + kBoundAbs;
+                wide = wide || !(fabsf(thr) < INFINITY) || second[q] <= thr;
+                const bool cand = best[q] <= thr;
+                const int key = cand ? bidx[q] * 16 + 4 * g : 0x7fffffff;
+                cbase[q] = lanes_min_int(key);
+                multi = multi || (cand && key != cbase[q]);
             }
 
             // ---- pass 2: direct distances of the candidates
@@ -273,9 +289,24 @@ __global__ __launch_bounds__(kMfThreads) void encode_mfma_kernel(
                 for (int bb = 0; bb < kMfBlocks; ++bb)
 #pragma unroll
                     for (int q = 0; q < NG; ++q) direct_scan_group(xs[q], rm, bb * 16 + 4 * g, bd[q], bi[q]);
-            } else {
+            } else if (__any(multi)) {
+                // every lane scans its best group (those of lanes that are not
+                // candidates hold no winner, and lose to one that does)
 #pragma unroll
                 for (int q = 0; q < NG; ++q) direct_scan_group(xs[q], rm, bidx[q] * 16 + 4 * g, bd[q], bi[q]);
+            } else {
+                // one candidate group per token: its 4 lanes take one centroid each
+#pragma unroll
+                for (int q = 0; q < NG; ++q) {
+                    const int c = cbase[q] + g;
+                    const float* r = rm + (c >> 4) * W + (c & 15);
+                    float cv[kMfDsub];
+#pragma unroll
+                    for (int k = 0; k < kMfDsub; ++k) cv[k] = r[16 * k];
+                    const float dd = sq_dist<kMfDsub>(xs[q], cv);
+                    bd[q] = dd < INFINITY ? dd : INFINITY;  // NaN: never the winner
+                    bi[q] = c;
+                }
             }
 #pragma unroll
             for (int q = 0; q < NG; ++q) {
