@@ -6,7 +6,8 @@ benchmark's ``cpu_baseline`` leg may import this package.  The product path
 it shares no code with that path: the only thing both sides share is the
 seeded input generator ``synthkv``.
 
-Precision: float64 throughout, from exact widenings of the fp16/fp32 inputs.
+Precision: float64 throughout, from exact widenings of the fp16/fp32 inputs,
+except ``encode_f32`` (see O2).
 
 What it computes, and where the page (the MILLION write-up, DAC 2025)
 states it:
@@ -17,6 +18,8 @@ states it:
   trained offline).
 * O2  ``encode`` -- brute-force nearest centroid (Fig. 6 paragraph: the online
   prefill stage quantises the KV cache with the trained codebooks).
+  ``encode_f32`` takes the same decision in fp32, the precision of the GPU path,
+  so that codes can be compared byte for byte, near ties included.
 * O3/O4 ``decode_exact`` -- dequantise, then plain softmax attention over
   history + recent tokens (Fig. 7 paragraph: history attention and
   generated-token attention are computed separately and combined; their union
@@ -57,7 +60,9 @@ AMBIGUITY_REL = 1e-5
 
 def build(verbose: bool = False) -> str:
     """Compile oracle.c with gcc into liboracle.so (always recompiles)."""
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-o", _LIB + ".tmp", _SRC, "-lm"]
+    # no contraction: every fp32 step of encode_f32 rounds exactly as written
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-o",
+           _LIB + ".tmp", _SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -82,6 +87,9 @@ def lib():
         L.orc_fit_codebooks.argtypes = [p, i64, i32, i32, i32, i32, i32, p, p, p]
         L.orc_encode.argtypes = [p, i64, i32, i32, i32, i32, p, p, p, p]
         L.orc_code_distance.argtypes = [p, i64, i32, i32, i32, i32, p, p, p]
+        L.orc_encode_f32.argtypes = [p, i64, i32, i32, i32, i32, p, p]
+        L.orc_sqdist_f32.argtypes = [p, p, i32]
+        L.orc_sqdist_f32.restype = ctypes.c_float
         L.orc_decode_exact.argtypes = [i32, i32, i32, i32, i32, i32, p, p, p, p, p, i64, p, p, p, i64, p,
                                        f64, p, p]
         L.orc_dequantize.argtypes = [p, i64, i32, i32, i32, i32, p, p]
@@ -177,6 +185,34 @@ def encode(x, codebook):
     if rc != 0:
         raise ValueError("bad encode arguments")
     return codes, d1, d2, ambiguous(d1, d2)
+
+
+def encode_f32(x, codebook):
+    """The same nearest-centroid rule, decided in fp32 (O2 in the precision the GPU
+    computes in: a code is an integer that floating point decides, and the page
+    fixes no precision).  The squared distance is evaluated in subspace order:
+    e = x_j - c_j rounded to fp32, then d = fma(e, e, d) from d = 0.  The first
+    centroid with a strictly smaller d wins (lowest index on ties); a NaN distance
+    never wins; no distance below +inf gives code 0.
+
+    x: [N, H, d] fp16/fp32; codebook: [H, K, M, d_sub] fp32.  Returns uint8 [N, H, M]."""
+    X = _f32(x)
+    cb = _f32(codebook)
+    N, H, d = X.shape
+    Hc, K, M, d_sub = cb.shape
+    assert Hc == H and M * d_sub == d
+    codes = np.empty((N, H, M), np.uint8)
+    if lib().orc_encode_f32(_ptr(X), N, H, d, d_sub, K, _ptr(cb), _ptr(codes)) != 0:
+        raise ValueError("bad encode arguments")
+    return codes
+
+
+def sqdist_f32(x, c) -> float:
+    """encode_f32's distance of one subvector x to one centroid c (fp32)."""
+    x = _f32(x).ravel()
+    c = _f32(c).ravel()
+    assert x.size == c.size
+    return float(lib().orc_sqdist_f32(_ptr(x), _ptr(c), int(x.size)))
 
 
 def ambiguous(d1, d2):

@@ -223,6 +223,53 @@ int orc_encode(const float *x, int64_t N, int H, int d, int dsub, int K, const f
     return 0;
 }
 
+/* O2 in fp32: the same nearest-centroid rule, decided in single precision.  */
+/* A code is an integer that floating point decides; the page fixes no      */
+/* precision, so this is the decision in the precision the GPU computes in:   */
+/* the squared distance evaluated in subspace order, e_j = x_j - c_j rounded  */
+/* to fp32, then d = fma(e_j, e_j, d) from d = 0 (one rounding per term).     */
+/* The first centroid with a strictly smaller d than every earlier one wins   */
+/* (lowest index on ties); a NaN distance never wins, and a subvector with   */
+/* no distance below +inf gets code 0.                                        */
+static float sqdist_f32(const float *x, const float *c, int dsub) {
+    float s = 0.0f;
+    for (int j = 0; j < dsub; ++j) {
+        const float e = x[j] - c[j];
+        s = fmaf(e, e, s);
+    }
+    return s;
+}
+
+float orc_sqdist_f32(const float *x, const float *c, int dsub) { return sqdist_f32(x, c, dsub); }
+
+int orc_encode_f32(const float *x, int64_t N, int H, int d, int dsub, int K, const float *cb, uint8_t *codes) {
+    if (d % dsub || K < 1 || K > 256 || dsub > 8) return -1;
+    const int M = d / dsub;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t u = 0; u < (int64_t)H * M; ++u) {
+        const int h = (int)(u / M), m = (int)(u % M);
+        float *C = (float *)malloc(sizeof(float) * K * dsub);
+        for (int c = 0; c < K; ++c)
+            for (int j = 0; j < dsub; ++j) C[c * dsub + j] = cb[(((int64_t)h * K + c) * M + m) * dsub + j];
+        float p[8];
+        for (int64_t t = 0; t < N; ++t) {
+            for (int j = 0; j < dsub; ++j) p[j] = x[(t * H + h) * d + m * dsub + j];
+            float best = INFINITY;
+            int code = 0;
+            for (int c = 0; c < K; ++c) {
+                const float dc = sqdist_f32(p, C + c * dsub, dsub);
+                if (dc < best) {
+                    best = dc;
+                    code = c;
+                }
+            }
+            codes[(t * H + h) * M + m] = (uint8_t)code;
+        }
+        free(C);
+    }
+    return 0;
+}
+
 /* Distance of given codes (e.g. another implementation's), fp64, [N][H][M]. */
 int orc_code_distance(const float *x, int64_t N, int H, int d, int dsub, int K, const float *cb,
                       const uint8_t *codes, double *dist) {

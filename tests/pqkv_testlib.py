@@ -99,7 +99,17 @@ def run_gpu_encode(dims, x, codebook, n_seqs_planes, t_cap, t_start=0, init_code
 
 
 def check_codes(gpu_codes, x, codebook, ref_codes, d1, d2):
-    """gpu_codes/ref_codes logical [N, H, M]; returns (n_ambiguous, n_total)."""
+    """gpu_codes/ref_codes logical [N, H, M]; returns (n_ambiguous, n_total).
+
+    Every code must be the oracle's fp32 decision (encode_f32), byte for byte, near
+    ties included.  Against the fp64 decision (ref_codes, best and runner-up distances
+    d1, d2): equal outside the 1e-5 band, and inside it the GPU code's fp64 distance
+    within the band of the best."""
+    c32 = oracle.encode_f32(x, codebook)
+    diff = gpu_codes != c32
+    if diff.any():
+        idx = np.argwhere(diff)[:5]
+        raise AssertionError(f"{int(diff.sum())} codes differ from the fp32 decision, first at {idx.tolist()}")
     amb = oracle.ambiguous(d1, d2)
     ok = ~amb
     mism = (gpu_codes != ref_codes) & ok

@@ -8,6 +8,7 @@ the oracle (a dropped term, a wrong sign or index, a transposed operand) should
 fail at least one of them.
 """
 import itertools
+from fractions import Fraction
 import json
 import math
 import os
@@ -295,6 +296,109 @@ def test_code_distance_consistent(oracle_mod):
     np.testing.assert_array_equal(oracle.code_distance(x, cb, codes), d1)
     other = (codes.astype(int) + 1) % 8
     assert np.all(oracle.code_distance(x, cb, other.astype(np.uint8)) >= d1)
+
+
+# ------------------------------------------------------------------ O2 encode, fp32 decision
+def _round_f32(q: Fraction) -> float:
+    """An exact rational rounded to the nearest fp32 value, ties to even (IEEE 754
+    round-to-nearest), returned as a Python float (exact)."""
+    if q == 0:
+        return 0.0
+    sign = -1.0 if q < 0 else 1.0
+    a = -q if q < 0 else q
+    e = a.numerator.bit_length() - a.denominator.bit_length()  # floor(log2 a) or one above
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)  # subnormals: the smallest normal exponent, fewer significant bits
+    scale = Fraction(2) ** (23 - e)
+    m = a * scale
+    n = m.numerator // m.denominator
+    r = m - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = Fraction(n) / scale
+    if v >= Fraction(2) ** 128:
+        return sign * math.inf
+    return sign * float(v)
+
+
+def _sqdist_f32_exact(x, c) -> float:
+    """fp32 squared distance from exact arithmetic: each difference rounded to fp32, each
+    square added to the running sum with one rounding (a fused multiply-add)."""
+    d = Fraction(0)
+    for a, b in zip(x, c):
+        e = _round_f32(Fraction(float(a)) - Fraction(float(b)))
+        d = Fraction(_round_f32(Fraction(e) * Fraction(e) + d))
+    return float(d)
+
+
+def test_encode_f32_distance_is_exactly_rounded(oracle_mod):
+    """The fp32 distance, against exact rational arithmetic rounded to fp32 at each step,
+    over magnitudes from 1e-3 to 1e3 (including cancellation and exact zeros)."""
+    rng = np.random.default_rng(21)
+    for dsub in (2, 4):
+        for _ in range(400):
+            mag = 10.0 ** rng.uniform(-3, 3)
+            x = (rng.standard_normal(dsub) * mag).astype(np.float32)
+            c = (x + rng.standard_normal(dsub).astype(np.float32) * np.float32(10.0 ** rng.uniform(-6, 0) * mag)
+                 ).astype(np.float32)
+            if rng.random() < 0.1:
+                c[0] = x[0]  # an exact zero difference
+            got = oracle.sqdist_f32(x, c)
+            assert got == _sqdist_f32_exact(x, c), (x, c)
+
+
+def test_encode_f32_bruteforce_tiny(oracle_mod):
+    """Codes: the first centroid with a strictly smaller fp32 distance, by brute force over
+    the exact-rounding model (with duplicate centroids, so exact ties occur)."""
+    rng = np.random.default_rng(22)
+    for dsub, K in ((2, 16), (4, 12)):
+        H, M = 2, 3
+        cb = rng.integers(-3, 4, size=(H, K, M, dsub)).astype(np.float32) * np.float32(0.5)
+        cb[:, K - 1] = cb[:, 2]  # a duplicate of centroid 2 at the end
+        x = (rng.integers(-6, 7, size=(40, H, M * dsub)) * 0.25).astype(np.float32)
+        got = oracle.encode_f32(x, cb)
+        for t in range(40):
+            for h in range(H):
+                for m in range(M):
+                    xs = x[t, h, m * dsub:(m + 1) * dsub]
+                    best, bd = 0, math.inf
+                    for c in range(K):
+                        dc = _sqdist_f32_exact(xs, cb[h, c, m])
+                        if dc < bd:
+                            best, bd = c, dc
+                    assert got[t, h, m] == best, (t, h, m)
+
+
+def test_encode_f32_equals_f64_outside_the_band(oracle_mod):
+    """Where the fp64 decision is clear (runner-up beyond the 1e-5 band), the fp32 decision
+    is the same code: outlier-bearing data, d_sub 2 and 4, 256 centroids."""
+    rng = np.random.default_rng(23)
+    for dsub in (2, 4):
+        x = rng.standard_normal((3000, 2, 32)).astype(np.float32)
+        x[:, :, 5] *= 10.0  # a channel outlier
+        x[rng.random(x.shape) < 0.005] *= 20.0  # point outliers
+        cb = rng.standard_normal((2, 256, 32 // dsub, dsub)).astype(np.float32)
+        c32 = oracle.encode_f32(x, cb)
+        c64, _, _, amb = oracle.encode(x, cb)
+        assert not ((c32 != c64) & ~amb).any()
+
+
+def test_encode_f32_special_cases(oracle_mod):
+    # a near tie that only fp32 rounding decides: |(1, 2^-13)|^2 = 1 + 2^-26 rounds to 1,
+    # so centroid 0 ties centroid 1 in fp32 and the lower index wins; fp64 picks 1
+    x = np.zeros((1, 1, 2), np.float32)
+    cb = np.array([[[[1.0, 2.0 ** -13]], [[1.0, 0.0]]]], np.float32)
+    assert oracle.encode_f32(x, cb)[0, 0, 0] == 0
+    assert oracle.encode(x, cb)[0][0, 0, 0] == 1
+    # exact duplicates: the lowest index
+    cb = np.array([[[[3.0, 1.0]], [[1.0, 1.0]], [[1.0, 1.0]]]], np.float32)
+    assert oracle.encode_f32(np.ones((1, 1, 2), np.float32), cb)[0, 0, 0] == 1
+    # a NaN centroid never wins; a NaN or infinite subvector gets code 0
+    cb = np.array([[[[np.nan, 0.0]], [[5.0, 5.0]], [[1.0, 1.0]]]], np.float32)
+    assert oracle.encode_f32(np.ones((1, 1, 2), np.float32), cb)[0, 0, 0] == 2
+    assert oracle.encode_f32(np.full((1, 1, 2), np.nan, np.float32), cb)[0, 0, 0] == 0
+    assert oracle.encode_f32(np.full((1, 1, 2), np.inf, np.float32), cb)[0, 0, 0] == 0
 
 
 # ------------------------------------------------------------------ O3/O4 attention
