@@ -78,7 +78,23 @@ def _encode_shapes(n=48, seed=77):
     return out
 
 
-@pytest.mark.parametrize("case", _encode_shapes(), ids=lambda c: f"d{c[0]}s{c[1]}K{c[2]}h{c[3]}n{c[4]}x{c[5]}")
+def _mfma_encode_shapes(seed=91):
+    """d_sub 4 with 256 centroids (the matrix-core encode): token counts at the edges of a
+    16-token group and of a work-group's 4096 tokens, and random ones."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i, N in enumerate((1, 15, 16, 17, 4095, 4096, 4097, int(rng.integers(5000, 20000)))):
+        d = (64, 128)[i % 2]
+        H = int(rng.integers(1, 9))
+        ns = int(rng.integers(1, 4)) if N < 5000 else 1
+        t_start = int(rng.integers(0, 100))
+        dt = np.float16 if i % 3 else np.float32
+        out.append((d, 4, 256, H, N, ns, t_start, dt, 5000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _encode_shapes() + _mfma_encode_shapes(),
+                         ids=lambda c: f"d{c[0]}s{c[1]}K{c[2]}h{c[3]}n{c[4]}x{c[5]}t{c[6]}")
 def test_random_shape_encode(case):
     d, dsub, K, H, N, ns, t_start, dt, seed = case
     M = d // dsub

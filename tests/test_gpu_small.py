@@ -132,6 +132,39 @@ def test_encode_nan_and_inf_rows(K):
     ref, _, _, _ = oracle.encode(x[0], cb)
     assert got[0, 3, 2] == 0 and np.all(got[0, 9] == 0)
     assert got[0, 3, 2] == ref[3, 0, 2] and np.array_equal(got[0, 9], ref[9, 0])
+    np.testing.assert_array_equal(got.transpose(1, 0, 2), oracle.encode_f32(x[0], cb))
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_encode_nonfinite_and_huge_centroids(d):
+    # d_sub 4, 256 centroids: a NaN centroid (never the code), an infinite one, and one
+    # whose |c|^2 overflows fp32, each in its own subspace; every code against the fp32
+    # decision
+    dsub, K, H = 4, 256, 2
+    M = d // dsub
+    cb = _codebook(21, H, K, M, dsub)
+    cb[0, 7, 1, 2] = np.nan
+    cb[1, 200, 3, 0] = np.inf
+    cb[0, 31, 5, :] = 3.0e19
+    x = _outlier_values(22, (1, 300, H, d), np.float32)
+    x[0, 5, 0, 5 * dsub:6 * dsub] = 2.9e19  # nearest to the huge centroid, at a finite fp32 distance
+    planes = run_gpu_encode(dims_for(d, dsub, K, H, H), x, cb, 1, 320)
+    got = oracle.untile_codes(planes[0], 300, M).transpose(1, 0, 2)
+    np.testing.assert_array_equal(got, oracle.encode_f32(x[0], cb))
+    assert np.all(got[:, 0, 1] != 7)
+
+
+@pytest.mark.parametrize("dsub", [4, 2])
+def test_encode_denormal_distances(dsub):
+    # values near 1e-20: squared distances in the fp32 denormal range, where the code
+    # depends on denormals being kept; every code against the fp32 decision
+    d, K, H = 64, 256, 1
+    M = d // dsub
+    cb = (_codebook(23, H, K, M, dsub) * np.float32(1e-20)).astype(np.float32)
+    x = (_outlier_values(24, (1, 500, H, d), np.float32) * np.float32(1e-20)).astype(np.float32)
+    planes = run_gpu_encode(dims_for(d, dsub, K, H, H), x, cb, 1, 512)
+    got = oracle.untile_codes(planes[0], 500, M).transpose(1, 0, 2)
+    np.testing.assert_array_equal(got, oracle.encode_f32(x[0], cb))
 
 
 def test_encode_deterministic():
