@@ -420,13 +420,19 @@ def main():
     enc_pairs = enc_tokens * Hkv * M * w.n_centroids  # (subvector, centroid) distance evaluations
     enc_flops = enc_pairs * (2 * w.d_sub)
     enc_tflops = enc_flops / (enc_total_ms * 1e-3) / 1e12
-    # VALU instructions per pair in the compiled scan (gfx950 asm of encode_kernel).  K a
-    # multiple of 64: d_sub subtractions and d_sub fused multiply-adds, half a min (a
-    # three-operand min tree per 16 centroids), a compare and two selects per 16 centroids,
-    # and the rescan of the winning 16 centroids (16 distances, compares and selects plus 4
-    # instructions per subvector).  Other K: the distance, a compare and two selects per
-    # pair, and loop bookkeeping (about 0.3 at d_sub 2, 0.6 at d_sub 4).
-    if w.n_centroids % 64 == 0:
+    # VALU instructions per pair.  The direct scan (encode_kernel), from its gfx950 asm: K a
+    # multiple of 64: d_sub subtractions and d_sub FMAs, half a min (a three-operand min tree
+    # per 16 centroids), a compare and two selects per 16 centroids, and the rescan of the
+    # winning 16 centroids (16 distances, compares and selects plus 4 instructions per
+    # subvector).  Other K: the distance, a compare and two selects per pair, and loop
+    # bookkeeping (about 0.3 at d_sub 2, 0.6 at d_sub 4).  The bounded expanded-form scan
+    # (encode_pruned_kernel, d_sub 2, K a multiple of 64): SQ_INSTS_VALU per pair on the 32K
+    # workload, 4.01 (its asm: 3.33 in the first pass; the rescans of the candidate
+    # sub-blocks, which depend on the data, and the per-subvector work make the rest).
+    pruned = w.d_sub == 2 and w.n_centroids % 64 == 0 and w.head_dim in (64, 128)
+    if pruned:
+        enc_ops_per_pair = 4.01
+    elif w.n_centroids % 64 == 0:
         enc_ops_per_pair = 2 * w.d_sub + 0.5 + 3 / 16 + (16 * (2 * w.d_sub + 2) + 4) / w.n_centroids
     else:
         enc_ops_per_pair = 2 * w.d_sub + 3 + (0.3 if w.d_sub == 2 else 0.6)
@@ -438,7 +444,8 @@ def main():
         encode = {"bound": "mfma", "kernel": "encode_mfma_kernel", "achieved": round(enc_tflops, 2),
                   "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(enc_tflops / FP32_MFMA_PEAK_TFLOPS, 4)}
     else:
-        encode = {"bound": "alu", "kernel": "encode_kernel", "valu_ops_per_pair": enc_ops_per_pair,
+        encode = {"bound": "alu", "kernel": "encode_pruned_kernel" if pruned else "encode_kernel",
+                  "pairs_per_s": round(enc_pairs / (enc_total_ms * 1e-3), 1), "valu_ops_per_pair": enc_ops_per_pair,
                   "achieved": round(enc_tops, 2), "peak": round(VALU_LANE_OPS_PEAK_T, 2), "unit": "T VALU lane-ops/s",
                   "frac": round(enc_tops / VALU_LANE_OPS_PEAK_T, 4), "flop_form_tflops": round(enc_tflops, 2),
                   "fp32_peak_tflops": FP32_VALU_PEAK_TFLOPS}

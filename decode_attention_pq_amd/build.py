@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libpqkv.so")
 # the decode kernel families come first: they take longest to compile
 DECODE_FAMILIES = ["decode_m64d2.hip", "decode_m64d2_lut.hip", "decode_m32d4.hip", "decode_m32d4_lut.hip",
                    "decode_m32d2.hip", "decode_m32d2_lut.hip", "decode_m16d4.hip", "decode_m16d4_lut.hip"]
-SOURCES = DECODE_FAMILIES + ["encode.hip", "encode_mfma.hip", "decode.hip", "aux_kernels.hip", "append.hip", "kmeans.hip", "noalloc.hip", "fp16_decode.hip",
+SOURCES = DECODE_FAMILIES + ["encode.hip", "encode_mfma.hip", "encode_pruned.hip", "decode.hip", "aux_kernels.hip", "append.hip", "kmeans.hip", "noalloc.hip", "fp16_decode.hip",
                             "api.cpp"]
 
 ARCH = "gfx950"

@@ -6,9 +6,10 @@
 // subvector is the index of the centroid at the smallest squared Euclidean
 // distance, the lowest index winning exact ties.
 //
-// This is the encode for d_sub 2 and for codebooks other than 256 centroids; at d_sub
-// 4 with 256 centroids the matrix cores narrow the scan down first (encode_mfma.hip)
-// and the same codes come out.
+// This is the encode for the shapes the two narrowing scans do not take: at d_sub 4
+// with 256 centroids the matrix cores narrow the scan down first (encode_mfma.hip),
+// and at d_sub 2 with a multiple of 64 centroids an error-bounded expanded-form scan
+// does (encode_pruned.hip); the same codes come out of both.
 //
 // Work decomposition (gfx950): one work-group of 1024 threads per (token block,
 // kv head, sequence).  The head's codebook (K x d fp32, at most 128 KiB) is staged
@@ -130,6 +131,9 @@ hipError_t launch_encode(const pqkv_dims& d, const void* x, pqkv_dtype xt, int32
     if (encode_mfma_supported(d))  // the same codes from the matrix cores (encode_mfma.hip)
         return launch_encode_mfma(d, x, xt, n_seqs, n_tokens, s_seq, s_tok, s_head, cb, codes, t_cap, t_start,
                                   stream);
+    if (encode_pruned_supported(d))  // the same codes from a bounded expanded-form scan (encode_pruned.hip)
+        return launch_encode_pruned(d, x, xt, n_seqs, n_tokens, s_seq, s_tok, s_head, cb, codes, t_cap, t_start,
+                                    stream);
     if (d.head_dim == 128 && d.d_sub == 2)
         return launch_dsub<128, 2>(d, x, xt, n_seqs, n_tokens, s_seq, s_tok, s_head, cb, codes, t_cap,
                                    t_start, stream);

@@ -24,6 +24,14 @@ hipError_t launch_encode_mfma(const pqkv_dims& d, const void* x, pqkv_dtype xt, 
                               const float* cb, uint8_t* codes, int64_t t_cap, int64_t t_start,
                               hipStream_t stream);
 
+// The error-bounded expanded-form scan (same arguments, same codes), for the shapes
+// encode_pruned_supported accepts (d_sub 2, a multiple of 64 centroids).
+bool encode_pruned_supported(const pqkv_dims& d);
+hipError_t launch_encode_pruned(const pqkv_dims& d, const void* x, pqkv_dtype xt, int32_t n_seqs,
+                                int64_t n_tokens, int64_t s_seq, int64_t s_tok, int64_t s_head,
+                                const float* cb, uint8_t* codes, int64_t t_cap, int64_t t_start,
+                                hipStream_t stream);
+
 hipError_t launch_build_lut(const pqkv_dims& d, int32_t batch, const void* q, pqkv_dtype qt,
                             const float* cb, float* lut, hipStream_t stream);
 
