@@ -242,6 +242,14 @@ __device__ inline void load4(const __half* p, float (&v)[4]) {
     v[3] = b.y;
 }
 
+#ifdef PQKV_TIMELINE
+// Probe builds only (tests/probes/decode_timeline.py): lane 0 of every wave writes
+// s_memrealtime stamps at the phase boundaries, and the work-group's XCC_ID and HW_ID
+// registers, to g_timeline[(work-group * 8 + wave) * 16 + k].  libpqkv itself is built
+// without it, and stamp() is then empty.
+__device__ unsigned long long* g_timeline;
+#endif
+
 // Issue priority of this wave on its SIMD (0-3).  The two waves of a SIMD would
 // otherwise be served oldest first, so the younger one falls behind in each phase and
 // the work-group then waits for it at the next barrier; a wave that is ahead by a
@@ -317,6 +325,19 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+#ifdef PQKV_TIMELINE
+    unsigned long long* tl = g_timeline ? g_timeline + ((size_t)blockIdx.x * kWaves + wave) * 16 : nullptr;
+    auto stamp = [&](int k) {
+        if (tl && lane == 0) tl[k] = __builtin_amdgcn_s_memrealtime();
+    };
+    stamp(0);
+    if (tl && lane == 0) {
+        tl[14] = (unsigned)__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (31 << 11));  // XCC_ID
+        tl[15] = (unsigned)__builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11));   // HW_ID
+    }
+#else
+    auto stamp = [](int) {};
+#endif
 
     // XCD-aware work mapping: work-group ids that share an XCD (id mod 8) take
     // contiguous items, so all splits of one kv head meet in one L2.  The grid has
@@ -495,6 +516,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     // would then wait for them too); the loads below also depend on the sequence
     // lengths, whose fetch the codebook loads overlap.
     __builtin_amdgcn_sched_barrier(0);
+    stamp(1);  // codebook requests issued
     int T_v = T_in, R_v = R_in;
     asm volatile("" : "+v"(T_v), "+v"(R_v));  // first use of the lengths: here, not earlier
     const int64_t T = clamp_hist(T_v);
@@ -611,13 +633,16 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     for (int k = 0; k < M / 2; ++k)
         ml[k] = 0x10000u | (uint32_t)(((2 * k + lane) & (M - 1)) * CS) |
                 ((uint32_t)(((2 * k + 1 + lane) & (M - 1)) * CS) << 8);
+    stamp(2);  // this wave's part of the LUT built
     __syncthreads();
+    stamp(3);  // phase 1 starts
 
     // ---- 3. phase 1: K codes -> scores (log2 domain)
     float sc[RW][QH];
 #pragma unroll
     for (int s = 0; s < RW; ++s) {
         set_prio(3 - (4 * s) / RW);
+        if (s == RW / 2) stamp(12);  // half of phase 1
         issue(ring[(s + P) % NSLOT], s + P);
 #pragma unroll
         for (int j = 0; j < QH; ++j) sc[s][j] = -INFINITY;
@@ -666,6 +691,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         }
     }
 
+    stamp(4);  // phase 1 ends
     set_prio(0);
     // ---- 4. work-group max over history and recent scores, and a bound on the
     //         history's weight sum, which sets the histogram's fixed-point scale: a
@@ -687,6 +713,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         }
     }
     __syncthreads();
+    stamp(5);  // the maxima have met
     // Fixed point: the history weights p = 2^(s - max) are added to the histogram as
     // round(p * 2^S), S the largest with L * 2^S < 2^31 for the bound L on the split's
     // weight sum (capped at 64).  A cell, and the split's sum, then stay below 2^31
@@ -773,6 +800,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int s = RW; s < 2 * RW; ++s) {
         set_prio(3 - (4 * (s - RW)) / RW);
+        if (s == RW + RW / 2) stamp(13);  // half of phase 2
         if (s + P < 2 * RW) issue(ring[(s + P) % NSLOT], s + P);  // nothing is left to request at the end
         if (step_ok(s) && step_tile(s) * kTileTokens + lane < t1) {
             const u32x4(&cw)[NCH] = ring[s % NSLOT];
@@ -810,6 +838,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
             }
         }
     }
+    stamp(6);  // phase 2 ends
     set_prio(0);
     // recent weights, scaled by 2^S like the histogram
 #pragma unroll
@@ -828,6 +857,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         }
     }
     __syncthreads();
+    stamp(7);  // the histogram is complete
 
     // ---- 6. output partial: histogram x value codebook + recent weights x values
     // partial records: one per (item, query head of the group), item = item_first + split
@@ -898,6 +928,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
 #pragma unroll
             for (int i = 0; i < CPL; ++i) ored[(wave * QH + j) * D + em * DSUB + ecomp + i] = acc[j][i];
     }
+    stamp(8);  // epilogue done
     __syncthreads();
     if (ns == 1) {
         // The unit's only split: it normalises its own output, with no partial
@@ -967,11 +998,13 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     // increment that follows is therefore ordered after all of them.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    stamp(9);  // partial published
     if (tid == 0) {
         const uint32_t done = __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last_flag = (done == (uint32_t)(ns - 1));
     }
     __syncthreads();
+    stamp(10);  // counter returned
     if (!last_flag) return;
     // Every output element reads (max, sum, value) of eight splits at a time --
     // all loads in flight together -- and folds them in with a running max.
@@ -1020,6 +1053,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         if (el == 0) a.lse[orow] = (mall + log2f(l)) * kLn2;
     }
     if (tid == 0) __hip_atomic_store(a.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stamp(11);  // merge done
 }
 
 template <int M, int DSUB, int QH, int RW, bool EXT, typename QT, typename RT>
