@@ -117,6 +117,33 @@ def test_encode_ties_at_dsub4(d, keep, dups):
     check_codes(got, x2, cb2, ref, d1, d2)
 
 
+@pytest.mark.parametrize("keep,dups", [(70, (130, 200, 255)), (17, (16, 18, 19)), (240, (0, 241)),
+                                       (5, (21,)), (100, (36, 164, 228))])
+@pytest.mark.parametrize("d", [128, 64])
+def test_encode_near_ties_at_dsub2(d, keep, dups):
+    # d_sub 2 with 256 centroids (the bounded expanded-form scan): copies of one centroid
+    # in its own and in other sub-blocks of 16, exact (the lowest index wins) and moved by
+    # a few ulp (near ties the bound cannot separate: the second or third best sub-block
+    # is rescanned, or the whole subspace); every code against the fp32 decision
+    dsub, K, H = 2, 256, 2
+    M = d // dsub
+    cb = _codebook(31 + keep, H, K, M, dsub)
+    for c in dups:
+        cb[:, c] = cb[:, keep]
+    x = np.repeat(cb[:, keep][None], 70, axis=0).reshape(70, H, d).astype(np.float32)
+    planes = run_gpu_encode(dims_for(d, dsub, K, H, H), x[None], cb, 1, 128)
+    got = oracle.untile_codes(planes[0], 70, M)
+    assert np.all(got == min((keep,) + tuple(dups)))
+    cb2 = cb.copy()
+    for n, c in enumerate(dups):
+        cb2[:, c, :, n % dsub] = np.nextafter(np.nextafter(cb[:, c, :, n % dsub], np.inf), np.inf)
+    x2 = x + np.float32(1e-3) * synthkv.small_normal(keep + 1, x.shape)
+    planes = run_gpu_encode(dims_for(d, dsub, K, H, H), x2[None], cb2, 1, 128)
+    got = oracle.untile_codes(planes[0], 70, M).transpose(1, 0, 2)
+    ref, d1, d2, _ = oracle.encode(x2, cb2)
+    check_codes(got, x2, cb2, ref, d1, d2)
+
+
 @pytest.mark.parametrize("K", [256, 40])
 def test_encode_nan_and_inf_rows(K):
     # a NaN subvector has no nearest centroid under '<': code 0, as in the oracle; an
