@@ -87,11 +87,13 @@ constexpr int kMfNg = 1;  // groups of 16 tokens a wave takes at a time
 // Minimum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the 4 lanes of a token).  A
 // permlane swap of a value with itself leaves each lane its own value and its
 // partner's, in an order that depends on the row; the minimum of the two does not.
-__device__ inline float lanes_min(float v) {
+// The minimum is a median against `ninf` (-inf, opaque to the compiler), which takes
+// no NaN-quieting moves on the swapped values.
+__device__ inline float lanes_min(float v, float ninf) {
     const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fminf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    v = __builtin_amdgcn_fmed3f(__uint_as_float(p[0]), __uint_as_float(p[1]), ninf);
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), ninf);
 }
 
 __device__ inline int lanes_min_int(int v) {
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(kMfThreads) void encode_mfma_kernel(
             int cbase[NG];
 #pragma unroll
             for (int q = 0; q < NG; ++q) {
-                const float thr = lanes_min(fmaf(kBound, xx[q] + fmaxf(best[q], 0.0f), best[q])) + kBoundAbs;
+                const float thr = lanes_min(fmaf(kBound, xx[q] + fmaxf(best[q], 0.0f), best[q]), ninf) + kBoundAbs;
                 wide = wide || !(fabsf(thr) < INFINITY) || second[q] <= thr;
                 const bool cand = best[q] <= thr;
                 const int key = cand ? bidx[q] * 16 + 4 * g : 0x7fffffff;
