@@ -8,7 +8,9 @@
 // tokens x 64 bytes) as 64-token tiles of 4 KiB, one 16-byte non-temporal load per lane
 // per 1 KiB chunk; a wave walks tiles wave, wave + 8, ... with three tiles in flight.
 // The grid reads 128 MiB per launch; launches rotate over 8 such buffers (1 GiB), so
-// no launch is served from the last-level cache.
+// no launch is served from the last-level cache.  The same kernel on 128, 32 and 8
+// work-groups (each still reading its 512 KiB) gives the rate one CU reaches when most
+// of the others are idle.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -84,6 +86,22 @@ int main() {
     const double us = best * 1e3 / kLaunches;
     std::printf("code-tile stream: %zu bytes per launch, %.2f us per launch (launch gaps included), %.1f GB/s, "
                 "%.1f%% of 8 TB/s\n", kBufBytes, us, kBufBytes / (us * 1e-6) / 1e9, kBufBytes / (us * 1e-6) / 8e12 * 100);
+    std::printf("  256 work-groups: %.1f GB/s per work-group\n", kGroupBytes / (us * 1e-6) / 1e9);
+    for (int groups : {128, 32, 8}) {  // the first `groups` slices of each buffer
+        float part = 1e30f;
+        for (int rep = 0; rep < 3; ++rep) {
+            if (hipEventRecord(e0) != hipSuccess) return 1;
+            for (int i = 0; i < kLaunches; ++i) stream<<<groups, kThreads>>>(buf[i % kBuffers], out);
+            if (hipGetLastError() != hipSuccess || hipEventRecord(e1) != hipSuccess || hipEventSynchronize(e1) != hipSuccess)
+                return 1;
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) return 1;
+            part = ms < part ? ms : part;
+        }
+        const double pus = part * 1e3 / kLaunches;
+        std::printf("  %3d work-groups: %.2f us per launch, %.1f GB/s in all, %.1f GB/s per work-group\n", groups, pus,
+                    groups * kGroupBytes / (pus * 1e-6) / 1e9, kGroupBytes / (pus * 1e-6) / 1e9);
+    }
     for (int i = 0; i < kBuffers; ++i) (void)hipFree(buf[i]);
     (void)hipFree(out);
     return 0;

@@ -41,6 +41,10 @@ def test_stream_rate_probe():
     out = _run("stream_rate")
     gbs = float(re.search(r"([\d.]+) GB/s", out).group(1))
     assert 500.0 < gbs < 8000.0, out
+    # one CU streams faster when most others are idle than its share of the full grid's rate
+    per = {int(g): float(r) for g, r in re.findall(r"(\d+) work-groups: .*?([\d.]+) GB/s per work-group", out)}
+    assert set(per) == {256, 128, 32, 8}, out
+    assert per[8] > per[256], out
 
 
 @pytest.mark.gpu
