@@ -1,12 +1,12 @@
 """Seeded sweeps of random decode and encode shapes against the oracle.
 
-Ninety-six decode shapes drawn from one seed cover the combinations the
+Four hundred and eighty decode shapes drawn from one seed cover the combinations the
 hand-written cases do not list: head size, subspace size, centroid count (2..256), kv and
 query heads (groups of 1, 2, 4 and 8), batch 1..5 with independent history
 lengths (empty, sub-tile, multi-split), recent windows from none to 300 rows,
 fp16 and fp32.  Every case runs the HIP decode through the C ABI and compares
-it with the dequantise-then-exact oracle at the usual tolerance.  Forty-eight
-encode shapes (head size, subspace size, centroid counts with and without whole
+it with the dequantise-then-exact oracle at the usual tolerance.  Two hundred and
+forty encode shapes (head size, subspace size, centroid counts with and without whole
 blocks of 64, 1..3 heads, 1..4999 tokens at a random start, one or two
 sequences, fp16 and fp32, outlier-heavy values) are compared code by code.
 """
@@ -20,7 +20,7 @@ from pqkv_testlib import check_attention, check_codes, dims_for, run_gpu_decode,
 pytestmark = pytest.mark.gpu
 
 
-def _shapes(n=96, seed=2024):
+def _shapes(n=480, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(n):
@@ -62,7 +62,7 @@ def test_random_shape_decode(case):
     check_attention(out, lse, ref_out, ref_lse)
 
 
-def _encode_shapes(n=48, seed=77):
+def _encode_shapes(n=240, seed=77):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
