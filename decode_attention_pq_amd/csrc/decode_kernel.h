@@ -244,9 +244,10 @@ __device__ inline void load4(const __half* p, float (&v)[4]) {
 
 #ifdef PQKV_TIMELINE
 // Probe builds only (tests/probes/decode_timeline.py): lane 0 of every wave writes
-// s_memrealtime stamps at the phase boundaries, and the work-group's XCC_ID and HW_ID
-// registers, to g_timeline[(work-group * 8 + wave) * 16 + k].  libpqkv itself is built
-// without it, and stamp() is then empty.
+// s_memrealtime stamps to g_timeline[(work-group * 8 + wave) * 48 + k]: k < 14 at the
+// phase boundaries, 14 and 15 the work-group's XCC_ID and HW_ID registers, 16 + s when
+// step s's code tile is in registers (s < 32; the stamp first waits for the whole
+// tile).  libpqkv itself is built without it, and stamp() and tile_ready() are empty.
 __device__ unsigned long long* g_timeline;
 #endif
 
@@ -326,9 +327,13 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
 #ifdef PQKV_TIMELINE
-    unsigned long long* tl = g_timeline ? g_timeline + ((size_t)blockIdx.x * kWaves + wave) * 16 : nullptr;
+    unsigned long long* tl = g_timeline ? g_timeline + ((size_t)blockIdx.x * kWaves + wave) * 48 : nullptr;
     auto stamp = [&](int k) {
-        if (tl && lane == 0) tl[k] = __builtin_amdgcn_s_memrealtime();
+        if (tl && lane == 0 && k < 48) tl[k] = __builtin_amdgcn_s_memrealtime();
+    };
+    auto tile_ready = [&](int s, const u32x4(&cw)[NCH]) {
+        asm volatile("" ::"v"(cw[0].x), "v"(cw[NCH - 1].w));
+        stamp(16 + s);
     };
     stamp(0);
     if (tl && lane == 0) {
@@ -337,6 +342,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
     }
 #else
     auto stamp = [](int) {};
+    auto tile_ready = [](int, const u32x4(&)[NCH]) {};
 #endif
 
     // XCD-aware work mapping: work-group ids that share an XCD (id mod 8) take
@@ -648,6 +654,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         for (int j = 0; j < QH; ++j) sc[s][j] = -INFINITY;
         if (step_ok(s)) {
             const u32x4(&cw)[NCH] = ring[s % NSLOT];
+            tile_ready(s, cw);
             float acc[QH][4];
 #pragma unroll
             for (int j = 0; j < QH; ++j)
@@ -804,6 +811,7 @@ __global__ __launch_bounds__(kThreads) void pq_decode_kernel(DecArgs a) {
         if (s + P < 2 * RW) issue(ring[(s + P) % NSLOT], s + P);  // nothing is left to request at the end
         if (step_ok(s) && step_tile(s) * kTileTokens + lane < t1) {
             const u32x4(&cw)[NCH] = ring[s % NSLOT];
+            tile_ready(s, cw);
             uint32_t p[QH];
 #pragma unroll
             for (int j = 0; j < QH; ++j) {

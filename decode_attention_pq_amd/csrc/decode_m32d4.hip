@@ -9,3 +9,10 @@ hipError_t launch_decode_m32d4(const pqkv_dims& d, int32_t batch, pqkv_dtype qt,
 }
 
 }  // namespace pqkv
+
+#ifdef PQKV_TIMELINE
+// Probe builds only: point the 32-subspace, d_sub 4 kernels' stamps at `buf` (NULL: off).
+extern "C" int pqkv_timeline_set_m32d4(void* buf) {
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(pqkv::g_timeline), &buf, sizeof(buf));
+}
+#endif

@@ -12,7 +12,7 @@ hipError_t launch_decode_m64d2(const pqkv_dims& d, int32_t batch, pqkv_dtype qt,
 
 #ifdef PQKV_TIMELINE
 // Probe builds only: point the 64-subspace kernels' stamps at `buf` (NULL: off).
-extern "C" int pqkv_timeline_set(void* buf) {
+extern "C" int pqkv_timeline_set_m64d2(void* buf) {
     return (int)hipMemcpyToSymbol(HIP_SYMBOL(pqkv::g_timeline), &buf, sizeof(buf));
 }
 #endif

@@ -48,19 +48,20 @@ def test_stream_rate_probe():
 
 
 @pytest.mark.gpu
-def test_decode_timeline_probe():
-    """The per-phase timeline of a 32K decode call (libpqkv_timeline.so, stamps at the
-    phase boundaries of every wave), and the XCD of every work-group."""
+@pytest.mark.parametrize("shape,groups", [("32k", 256), ("gqa", 256), ("ragged", 512)])
+def test_decode_timeline_probe(shape, groups):
+    """The per-phase and per-step timeline of one decode call (libpqkv_timeline.so, stamps at
+    the phase boundaries and at every step of every wave), and the XCD of every work-group."""
     import sys
 
     script = os.path.join(HERE, "decode_timeline.py")
     if not os.path.exists(os.path.join(HERE, "libpqkv_timeline.so")):
         pytest.skip("libpqkv_timeline.so not built (tests/probes/build_probes.py)")
-    print("[probe] decode_timeline", flush=True)
-    r = subprocess.run([sys.executable, script], capture_output=True, text=True, timeout=300)
+    print(f"[probe] decode_timeline --shape {shape}", flush=True)
+    r = subprocess.run([sys.executable, script, "--shape", shape], capture_output=True, text=True, timeout=300)
     print(r.stdout, flush=True)
     assert r.returncode == 0, r.stdout + r.stderr
     m = re.search(r"XCC_ID == work-group id mod 8: (\d+) of (\d+)", r.stdout)
-    assert m and int(m.group(2)) == 256, r.stdout
+    assert m and int(m.group(2)) == groups, r.stdout
     # the XCD-aware mapping assumes the hardware deals work-groups out round-robin
     assert int(m.group(1)) == int(m.group(2)), r.stdout
