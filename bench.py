@@ -33,6 +33,10 @@ FP32_VALU_PEAK_TFLOPS = 157.3
 # The same peak in VALU lane-operations (one 32-bit VALU instruction on one lane, an FMA
 # counted once): 78.65 T/s.  The encode scan is counted in these units.
 VALU_LANE_OPS_PEAK_T = FP32_VALU_PEAK_TFLOPS / 2
+# That peak counts packed fp32 instructions (two lane-operations each).  The kernels here are
+# built without packed fp32, so the rate they can issue is half of it: a wave64 instruction every
+# 4 clocks per SIMD, 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-operations/s.
+VALU_UNPACKED_ISSUE_T = VALU_LANE_OPS_PEAK_T / 2
 # dense fp32 matrix-core peak of MI355X (published), for the d_sub 4 encode
 FP32_MFMA_PEAK_TFLOPS = 157.3
 
@@ -447,7 +451,10 @@ def main():
         encode = {"bound": "alu", "kernel": "encode_pruned_kernel" if pruned else "encode_kernel",
                   "pairs_per_s": round(enc_pairs / (enc_total_ms * 1e-3), 1), "valu_ops_per_pair": enc_ops_per_pair,
                   "achieved": round(enc_tops, 2), "peak": round(VALU_LANE_OPS_PEAK_T, 2), "unit": "T VALU lane-ops/s",
-                  "frac": round(enc_tops / VALU_LANE_OPS_PEAK_T, 4), "flop_form_tflops": round(enc_tflops, 2),
+                  "frac": round(enc_tops / VALU_LANE_OPS_PEAK_T, 4),
+                  "unpacked_issue_peak": round(VALU_UNPACKED_ISSUE_T, 2),
+                  "frac_of_unpacked_issue": round(enc_tops / VALU_UNPACKED_ISSUE_T, 4),
+                  "flop_form_tflops": round(enc_tflops, 2),
                   "fp32_peak_tflops": FP32_VALU_PEAK_TFLOPS}
 
     result = {
