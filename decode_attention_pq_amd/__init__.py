@@ -14,7 +14,7 @@ import os
 import torch  # loads the HIP runtime libpqkv.so binds to (same soname)
 
 __all__ = [
-    "PQKVError", "Dims", "lib", "LIB_PATH", "encode", "build_lut", "decode_workspace_bytes",
+    "PQKVError", "Dims", "lib", "LIB_PATH", "encode", "build_lut", "decode_workspace_bytes", "decode_plan", "DecodePlanInfo",
     "decode_attention", "fp16_decode_workspace_bytes", "fp16_decode_attention", "append_kv", "NOALLOC_SCRATCH_BYTES", "NOALLOC_MAX_ROWS", "fit_codebooks", "merge", "code_plane_bytes", "MAX_FIT_POINTS", "F16", "F32", "MAX_RECENT", "TILE_TOKENS",
 ]
 
@@ -49,6 +49,13 @@ class Dims(ctypes.Structure):
                 f"n_q_heads={self.n_q_heads}, n_kv_heads={self.n_kv_heads})")
 
 
+class DecodePlanInfo(ctypes.Structure):
+    """pqkv_decode_plan_info: the preset a decode call of given sizes runs."""
+    _fields_ = [("q_heads_per_group", ctypes.c_int32), ("splits", ctypes.c_int32), ("split_tokens", ctypes.c_int64),
+                ("rounds", ctypes.c_int32), ("build_rounds", ctypes.c_int32), ("work_groups", ctypes.c_int64),
+                ("device_plan", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+
+
 _lib = None
 
 
@@ -67,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.pqkv_build_lut.restype = i32
         L.pqkv_decode_workspace_bytes.argtypes = [dp, i32, i64]
         L.pqkv_decode_workspace_bytes.restype = sz
+        L.pqkv_decode_plan.argtypes = [dp, i32, i64, ctypes.POINTER(DecodePlanInfo)]
+        L.pqkv_decode_plan.restype = i32
         L.pqkv_decode_attention.argtypes = [dp, i32, vp, i32, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp, i32,
                                             i64, vp, f32, vp, vp, vp, sz, vp]
         L.pqkv_decode_attention.restype = i32
@@ -156,6 +165,13 @@ def build_lut(dims: Dims, q: torch.Tensor, codebook_k: torch.Tensor, lut: torch.
 
 def decode_workspace_bytes(dims: Dims, batch: int, max_hist_len: int) -> int:
     return int(lib().pqkv_decode_workspace_bytes(ctypes.byref(dims), batch, max_hist_len))
+
+
+def decode_plan(dims: Dims, batch: int, max_hist_len: int) -> dict:
+    """The preset pqkv_decode_attention runs for these sizes (pqkv_decode_plan), as a dict."""
+    info = DecodePlanInfo()
+    _check("pqkv_decode_plan", lib().pqkv_decode_plan(ctypes.byref(dims), batch, max_hist_len, ctypes.byref(info)))
+    return {name: int(getattr(info, name)) for name, _ in DecodePlanInfo._fields_}
 
 
 def _check_numel(name, t, n):

@@ -260,6 +260,26 @@ size_t pqkv_decode_workspace_bytes(const pqkv_dims* dims, int32_t batch, int64_t
     return plan_decode(*dims, batch, max_hist_len).workspace_bytes;
 }
 
+pqkv_status pqkv_decode_plan(const pqkv_dims* dims, int32_t batch, int64_t max_hist_len,
+                             pqkv_decode_plan_info* info) {
+    if (!dims || !info || batch <= 0 || max_hist_len < 0) return PQKV_ERR_INVALID;
+    const pqkv_status ds = check_dims(dims);
+    if (ds != PQKV_OK) return ds;
+    if ((int64_t)batch * dims->n_q_heads > 0x7fffffffLL) return PQKV_ERR_UNSUPPORTED;
+    const DecodePlan p = plan_decode(*dims, batch, max_hist_len);
+    if (p.n_split > kMaxSplits || p.units * p.n_split > 0x7fffffffLL - 8) return PQKV_ERR_UNSUPPORTED;
+    const int M = dims->head_dim / dims->d_sub;
+    info->q_heads_per_group = p.qh;
+    info->splits = p.n_split;
+    info->split_tokens = p.split_tokens;
+    info->rounds = p.rounds;
+    info->build_rounds = decode_kernel_rounds(M, p.qh, p.rounds);
+    info->work_groups = p.units * p.n_split;
+    info->device_plan = batch >= 2 && batch <= kDevicePlanMaxBatch && max_hist_len > 0 ? 1 : 0;
+    info->workspace_bytes = p.workspace_bytes;
+    return PQKV_OK;
+}
+
 pqkv_status pqkv_decode_attention(const pqkv_dims* dims, int32_t batch, const void* q,
                                   pqkv_dtype q_dtype, const float* lut, const float* codebook_k,
                                   const float* codebook_v, const uint8_t* codes_k,

@@ -131,6 +131,31 @@ pqkv_status pqkv_build_lut(const pqkv_dims* dims, int32_t batch, const void* q, 
 size_t pqkv_decode_workspace_bytes(const pqkv_dims* dims, int32_t batch, int64_t max_hist_len);
 
 /*
+ * The preset pqkv_decode_attention runs for these sizes: the kernel parameters that the
+ * Fig. 8 paragraph tunes per context length, here chosen at run time by a cost model over
+ * the split length and the kernel builds.  Host only: it reads no device memory and
+ * enqueues nothing.  For 2..16 sequences with a history the kernel re-plans the splits on
+ * the device from the actual lengths when they differ (device_plan = 1); the figures below
+ * are then the launched grid, which bounds that plan.
+ */
+typedef struct {
+    int32_t q_heads_per_group; /* query heads of one kv head per work-group: 1, 2 or 4 */
+    int32_t splits;            /* history splits per (sequence, kv head, head group); 1 without history */
+    int64_t split_tokens;      /* tokens per split, a multiple of 512; 0 without history */
+    int32_t rounds;            /* 512-token rounds per split: tiles per wave */
+    int32_t build_rounds;      /* tiles per wave of the kernel build that runs them */
+    int64_t work_groups;       /* work-groups launched, one per CU at a time */
+    int32_t device_plan;       /* 1: the kernel reads the lengths first and re-plans the splits
+                                  on the device when they differ */
+    size_t workspace_bytes;    /* pqkv_decode_workspace_bytes of the same sizes */
+} pqkv_decode_plan_info;
+
+/* Errors: INVALID for a null pointer, batch <= 0 or max_hist_len < 0; UNSUPPORTED for
+ * dims outside the ranges above or a history beyond what the merge's 512 splits cover. */
+pqkv_status pqkv_decode_plan(const pqkv_dims* dims, int32_t batch, int64_t max_hist_len,
+                             pqkv_decode_plan_info* info);
+
+/*
  * pqkv_decode_attention -- one decode step of attention for `batch` sequences
  * over a PQ-compressed history plus a recent full-precision window (Fig. 7
  * paragraph: history attention apart from new-token attention, ad-LUT scoring

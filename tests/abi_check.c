@@ -23,6 +23,17 @@ int main(void) {
     EXPECT(strcmp(pqkv_status_str(PQKV_OK), "ok") == 0);
     EXPECT(pqkv_decode_workspace_bytes(&d, 1, 32768) == (size_t)(32 * 8 * 132 * 4 + 256));
     EXPECT(pqkv_decode_workspace_bytes(&bad, 1, 32768) == 0);
+    {
+        pqkv_decode_plan_info pi;
+        memset(&pi, 0, sizeof(pi));
+        EXPECT(pqkv_decode_plan(&d, 1, 32768, &pi) == PQKV_OK);
+        EXPECT(pi.splits == 8 && pi.split_tokens == 4096 && pi.rounds == 8 && pi.build_rounds == 8);
+        EXPECT(pi.q_heads_per_group == 1 && pi.work_groups == 256 && pi.device_plan == 0);
+        EXPECT(pi.workspace_bytes == pqkv_decode_workspace_bytes(&d, 1, 32768));
+        EXPECT(pqkv_decode_plan(&d, 1, 32768, NULL) == PQKV_ERR_INVALID);
+        EXPECT(pqkv_decode_plan(&bad, 1, 32768, &pi) == PQKV_ERR_UNSUPPORTED);
+        EXPECT(pqkv_decode_plan(&d, 0, 32768, &pi) == PQKV_ERR_INVALID);
+    }
     EXPECT(pqkv_encode(&bad, fake, PQKV_F16, 1, 10, 0, 4096, 128, fake, fake, 64, 0, NULL) == PQKV_ERR_UNSUPPORTED);
     EXPECT(pqkv_encode(&d, NULL, PQKV_F16, 1, 10, 0, 4096, 128, fake, fake, 64, 0, NULL) == PQKV_ERR_INVALID);
     EXPECT(pqkv_encode(&d, NULL, PQKV_F16, 1, 0, 0, 4096, 128, NULL, NULL, 64, 0, NULL) == PQKV_OK);

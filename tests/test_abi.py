@@ -147,6 +147,53 @@ def test_split_plan_choices(P):
                                            None) == status
 
 
+def test_decode_plan_presets(P):
+    """pqkv_decode_plan: the preset a call runs, per context length (splits, split length,
+    kernel build, query heads per work-group), consistent with the workspace size and with
+    itself; the table over context lengths is printed."""
+    L = P.lib()
+    shapes = {"MHA d_sub 2 (32 heads x 128)": P.Dims(128, 2, 256, 32, 32),
+              "GQA d_sub 4 (32 over 8 heads)": P.Dims(128, 4, 256, 32, 8),
+              "GQA d_sub 4, head_dim 64 (16 over 4)": P.Dims(64, 4, 256, 16, 4)}
+    for name, dims in shapes.items():
+        M = dims.head_dim // dims.d_sub
+        g = dims.n_q_heads // dims.n_kv_heads
+        print(f"{name}: context -> splits x tokens, rounds / build, q heads per group, work-groups")
+        for batch in (1, 4, 16):
+            for T in (0, 64, 512, 4096, 8192, 32768, 131072, 1 << 20):
+                p = P.decode_plan(dims, batch, T)
+                if batch == 1:
+                    print(f"  batch {batch} T {T:8d}: {p['splits']:4d} x {p['split_tokens']:5d}, "
+                          f"{p['rounds']:2d} / {p['build_rounds']:2d}, {p['q_heads_per_group']}, {p['work_groups']}")
+                assert p["workspace_bytes"] == L.pqkv_decode_workspace_bytes(ctypes.byref(dims), batch, T)
+                qh = p["q_heads_per_group"]
+                assert qh in (1, 2, 4) and g % qh == 0 and qh * M <= 64
+                assert p["work_groups"] == batch * dims.n_kv_heads * (g // qh) * p["splits"]
+                assert p["device_plan"] == (1 if 2 <= batch <= 16 and T > 0 else 0)
+                if T == 0:
+                    assert p["splits"] == 1 and p["split_tokens"] == 0 and p["rounds"] == 0
+                    continue
+                assert p["split_tokens"] == 512 * p["rounds"]
+                # the splits cover the history, none of them empty
+                assert p["splits"] * p["split_tokens"] >= T > (p["splits"] - 1) * p["split_tokens"]
+                assert p["rounds"] <= p["build_rounds"] <= (8 if qh == 4 else 16)
+                assert p["build_rounds"] in ((2, 4, 8, 12, 16) if M == 64 else (4, 8, 16))
+    # the presets the workloads run
+    mha, gqa = shapes["MHA d_sub 2 (32 heads x 128)"], shapes["GQA d_sub 4 (32 over 8 heads)"]
+    assert {k: P.decode_plan(mha, 1, 32768)[k] for k in ("splits", "split_tokens", "work_groups")} == \
+        {"splits": 8, "split_tokens": 4096, "work_groups": 256}
+    assert {k: P.decode_plan(gqa, 1, 131072)[k] for k in ("q_heads_per_group", "splits", "split_tokens")} == \
+        {"q_heads_per_group": 2, "splits": 16, "split_tokens": 8192}
+    assert P.decode_plan(mha, 16, 8192)["splits"] == 1
+    # errors
+    info = P.DecodePlanInfo()
+    assert L.pqkv_decode_plan(ctypes.byref(mha), 1, 100, None) == 1
+    assert L.pqkv_decode_plan(ctypes.byref(mha), 0, 100, ctypes.byref(info)) == 1
+    assert L.pqkv_decode_plan(ctypes.byref(mha), 1, -1, ctypes.byref(info)) == 1
+    assert L.pqkv_decode_plan(_d(P, 96, 2, 256, 32, 32), 1, 100, ctypes.byref(info)) == 2
+    assert L.pqkv_decode_plan(_d(P, 128, 2, 256, 1, 1), 1, 5000000, ctypes.byref(info)) == 2  # > 512 splits
+
+
 def test_noalloc_refuses_sizes_beyond_its_array(P):
     """pqkv_decode_attention_noalloc checks on the host that the call fits its static
     array (rows of counters, then partials) before it touches a device."""
