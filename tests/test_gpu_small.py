@@ -544,3 +544,40 @@ def test_decode_large_magnitudes(dsub):
     out, lse = run_gpu_decode(dims_for(d, dsub, K, Hq, Hkv), q, cbk, cbv, oracle.tile_codes(ck, t_cap),
                               oracle.tile_codes(cv, t_cap), t_cap, hist, rk, rv, rec, scale)
     check_attention(out, lse, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("dsub,K", [(2, 256), (4, 256), (2, 100)], ids=["bounded-scan", "matrix-core", "direct-scan"])
+def test_encode_strided_input(dsub, K):
+    """Every encode kernel reads x through its strides: a view that skips every other token
+    and whose head rows are padded (as a slice of a wider projection output) gives the codes
+    of the contiguous copy, byte for byte, and those are the fp32 decision."""
+    import torch
+
+    import decode_attention_pq_amd as P
+
+    d, H, N, ns = 128, 3, 1500, 2
+    M = d // dsub
+    t_cap = -(-N // 64) * 64
+    rng = np.random.default_rng(4100 + K + dsub)
+    x = rng.standard_normal((ns, N, H, d)).astype(np.float32)
+    x[..., :3] *= 10.0
+    x[rng.random(x.shape) < 0.01] *= 20.0
+    x = x.astype(np.float16)
+    cb = (np.random.default_rng(4200 + K).standard_normal((H, K, M, dsub)) * 3).astype(np.float32)
+    dims = dims_for(d, dsub, K, H, H)
+    wide = np.zeros((ns, 2 * N, H, d + 8), np.float16)
+    wide[:, ::2, :, :d] = x
+    view = to_dev(wide)[:, ::2, :, :d]
+    assert not view.is_contiguous() and view.stride(1) == 2 * H * (d + 8) and view.stride(2) == d + 8
+    cbd = to_dev(cb)
+    planes = []
+    for xin in (view, to_dev(x)):
+        codes = torch.zeros((ns, H, t_cap * M), dtype=torch.uint8, device="cuda")
+        P.encode(dims, xin, cbd, codes, t_cap)
+        torch.cuda.synchronize()
+        planes.append(codes.cpu().numpy())
+    assert np.array_equal(planes[0], planes[1])
+    for s in range(ns):
+        ref, d1, d2, _ = oracle.encode(x[s], cb)
+        got = oracle.untile_codes(planes[0][s], N, M).transpose(1, 0, 2)
+        check_codes(got, x[s], cb, ref, d1, d2)
