@@ -581,3 +581,29 @@ def test_encode_strided_input(dsub, K):
         ref, d1, d2, _ = oracle.encode(x[s], cb)
         got = oracle.untile_codes(planes[0][s], N, M).transpose(1, 0, 2)
         check_codes(got, x[s], cb, ref, d1, d2)
+
+
+@pytest.mark.parametrize("hist,t_cap", [((3000,), 32768), ((100, 0, 7000), 20480), ((9000, 9000), 65536)],
+                         ids=["one-sequence", "ragged", "equal-lengths"])
+def test_decode_with_capacity_as_max_hist(hist, t_cap):
+    """A serving loop passes its cache capacity as max_hist_len: the plan is then sized for
+    the capacity, most splits hold no tokens and leave at once (one sequence), or the
+    device-side plan resizes them from the actual lengths (2..16 sequences); the result is
+    the attention over the actual lengths."""
+    d, dsub, K, Hq, Hkv, R = 128, 2, 256, 8, 4, 16
+    B, M = len(hist), d // dsub
+    seed = 900 + sum(hist) + t_cap
+    q = synthkv.small_normal(seed, (B, Hq, d), np.float16)
+    cbk = _codebook(seed + 1, Hkv, K, M, dsub, 1.0)
+    cbv = _codebook(seed + 2, Hkv, K, M, dsub, 1.0)
+    ck = synthkv.small_codes(seed + 3, (B, Hkv, t_cap, M), K)
+    cv = synthkv.small_codes(seed + 4, (B, Hkv, t_cap, M), K)
+    rk = synthkv.small_normal(seed + 5, (B, Hkv, R, d), np.float16)
+    rv = synthkv.small_normal(seed + 6, (B, Hkv, R, d), np.float16)
+    rec = tuple(R - i for i in range(B))
+    scale = softmax_scale(d)
+    ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, hist, rk, rv, rec, scale)
+    dims = dims_for(d, dsub, K, Hq, Hkv)
+    out, lse = run_gpu_decode(dims, q, cbk, cbv, oracle.tile_codes(ck, t_cap), oracle.tile_codes(cv, t_cap), t_cap,
+                              hist, rk, rv, rec, scale, max_hist=t_cap)
+    check_attention(out, lse, ref_out, ref_lse)
