@@ -607,3 +607,28 @@ def test_decode_with_capacity_as_max_hist(hist, t_cap):
     out, lse = run_gpu_decode(dims, q, cbk, cbv, oracle.tile_codes(ck, t_cap), oracle.tile_codes(cv, t_cap), t_cap,
                               hist, rk, rv, rec, scale, max_hist=t_cap)
     check_attention(out, lse, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("qdt,rdt", [(np.float16, np.float32), (np.float32, np.float16)], ids=["q16-r32", "q32-r16"])
+@pytest.mark.parametrize("dsub,Hq,Hkv", [(2, 4, 4), (4, 8, 4)], ids=["mha-dsub2", "gqa-dsub4"])
+def test_decode_mixed_q_and_recent_dtypes(qdt, rdt, dsub, Hq, Hkv):
+    """q and the recent window take their dtypes independently (every combination is its
+    own kernel build)."""
+    d, K, R = 128, 256, 40
+    hist, rec = (5000, 700), (40, 13)
+    B, M = len(hist), d // dsub
+    t_cap = -(-max(hist) // 64) * 64
+    seed = 7100 + dsub + Hq
+    q = synthkv.small_normal(seed, (B, Hq, d), qdt)
+    cbk = _codebook(seed + 1, Hkv, K, M, dsub, 1.0)
+    cbv = _codebook(seed + 2, Hkv, K, M, dsub, 1.0)
+    ck = synthkv.small_codes(seed + 3, (B, Hkv, t_cap, M), K)
+    cv = synthkv.small_codes(seed + 4, (B, Hkv, t_cap, M), K)
+    rk = synthkv.small_normal(seed + 5, (B, Hkv, R, d), rdt)
+    rv = synthkv.small_normal(seed + 6, (B, Hkv, R, d), rdt)
+    scale = softmax_scale(d)
+    ref_out, ref_lse = oracle.decode_exact(q, cbk, cbv, ck, cv, hist, rk, rv, rec, scale)
+    dims = dims_for(d, dsub, K, Hq, Hkv)
+    out, lse = run_gpu_decode(dims, q, cbk, cbv, oracle.tile_codes(ck, t_cap), oracle.tile_codes(cv, t_cap), t_cap,
+                              hist, rk, rv, rec, scale)
+    check_attention(out, lse, ref_out, ref_lse)
